@@ -1,0 +1,95 @@
+"""Seeded synthetic inputs for the DF-SSM scaffold projection.
+
+This module only draws random numbers: it holds none of the projection's
+arithmetic (no quantization, no sign packing, no products), so both the HIP
+path's tests/benchmark and the CPU oracle can consume the same buffers.
+
+Shapes follow the Mamba-2 1.3B layout the pages name (DF-SSM technical summary,
+section 2B: LoRA on in_proj and out_proj of all 48 layers; d_model 2048,
+d_inner 4096, in_proj width 2*4096 + 2*128 + 64 = 8512).  Distributions:
+sign bits are uniform random bytes (iid Bernoulli(1/2) signs), the scaffold
+scale s_w ~ U[0.01, 0.05], activations x ~ N(0, 1) fp32 with a few outlier
+input channels scaled by 20, LoRA matrices uniform int8 in [-127, 127] with
+per-row scales ~ U[1e-4, 1e-3].
+
+Draw order per problem (numpy PCG64 via default_rng(seed)):
+  1. P   = integers(0, 256, (N, K/8), uint8)
+  2. s_w = uniform(0.01, 0.05, N)           -> float32
+  3. x   = standard_normal((M, K), float32)
+  4. idx = choice(K, n_outliers, replace=False); x[:, idx] *= 20
+  5. W_A = integers(-127, 128, (N, r), int8), s_A = uniform(1e-4, 1e-3, N)
+  6. W_B = integers(-127, 128, (r, K), int8), s_B = uniform(1e-4, 1e-3, r)
+Further copies (rotated weight sets) continue the same generator stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+RANK = 16
+
+
+@dataclass
+class Problem:
+    """One projection's inputs (host numpy arrays)."""
+    x: np.ndarray      # float32 [M, K]
+    P: np.ndarray      # uint8   [N, K/8]  sign bits, LSB = lowest k, 1 = +1
+    s_w: np.ndarray    # float32 [N]
+    W_A: np.ndarray    # int8    [N, r]
+    s_A: np.ndarray    # float32 [N]
+    W_B: np.ndarray    # int8    [r, K]
+    s_B: np.ndarray    # float32 [r]
+
+    @property
+    def M(self):
+        return self.x.shape[0]
+
+    @property
+    def K(self):
+        return self.x.shape[1]
+
+    @property
+    def N(self):
+        return self.P.shape[0]
+
+
+def draw_problem(rng: np.random.Generator, M: int, N: int, K: int, n_outliers: int,
+                 rank: int = RANK) -> Problem:
+    if K % 8:
+        raise ValueError("K must be a multiple of 8")
+    P = rng.integers(0, 256, (N, K // 8), dtype=np.uint8)
+    s_w = rng.uniform(0.01, 0.05, N).astype(np.float32)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    if n_outliers:
+        idx = rng.choice(K, n_outliers, replace=False)
+        x[:, idx] *= np.float32(20.0)
+    W_A = rng.integers(-127, 128, (N, rank), dtype=np.int8)
+    s_A = rng.uniform(1e-4, 1e-3, N).astype(np.float32)
+    W_B = rng.integers(-127, 128, (rank, K), dtype=np.int8)
+    s_B = rng.uniform(1e-4, 1e-3, rank).astype(np.float32)
+    return Problem(x, P, s_w, W_A, s_A, W_B, s_B)
+
+
+def make_problem(M: int, N: int, K: int, n_outliers: int, seed: int, rank: int = RANK) -> Problem:
+    return draw_problem(np.random.default_rng(seed), M, N, K, n_outliers, rank)
+
+
+def make_copies(M: int, N: int, K: int, n_outliers: int, seed: int, copies: int,
+                rank: int = RANK) -> list[Problem]:
+    """`copies` independent problems drawn back to back from one seeded stream."""
+    rng = np.random.default_rng(seed)
+    return [draw_problem(rng, M, N, K, n_outliers, rank) for _ in range(copies)]
+
+
+# The five workloads: (name, list of (M, N, K, n_outliers), seed)
+CONFIGS = {
+    "tiny_m1_k256_n512": dict(shapes=[(1, 512, 256, 2)], seed=0),
+    "out_proj_decode_m1_k4096_n2048": dict(shapes=[(1, 2048, 4096, 2)], seed=1),
+    "in_proj_decode_k2048_n8512": dict(shapes=[(1, 8512, 2048, 2), (4, 8512, 2048, 2),
+                                               (16, 8512, 2048, 2)], seed=2),
+    # 48 layers x (in_proj K2048->N8512, out_proj K4096->N2048), fresh N(0,1) inputs
+    "decode_sweep_48l": dict(shapes=[(1, 8512, 2048, 0), (1, 2048, 4096, 0)], seed=3, layers=48),
+    # prefill: 1 % outlier channels (round(0.01 K)) -> 20 at K 2048, 41 at K 4096
+    "prefill_m2048": dict(shapes=[(2048, 8512, 2048, 20), (2048, 2048, 4096, 41)], seed=4),
+}
