@@ -9,29 +9,105 @@
 namespace dfssm {
 hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int8_t* x_q, float* s_x,
                                hipStream_t stream);
+int quantize_lora_tokens_per_group(int64_t K);
+hipError_t launch_quantize_lora_down(const float* x, int64_t M, int64_t K, const int8_t* w_b, int rank,
+                                     int8_t* x_q, float* s_x, int32_t* t, int64_t batch, hipStream_t stream);
 hipError_t launch_lora_down(const int8_t* x_q, int64_t M, int64_t K, const int8_t* w_b, int32_t* t,
-                            hipStream_t stream);
+                            int64_t batch, hipStream_t stream);
 hipError_t launch_gemv(const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
                        const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
                        const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                       hipStream_t stream);
+                       int64_t batch, hipStream_t stream);
 hipError_t launch_gemm_mfma(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                             const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
                             const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                            hipStream_t stream);
+                            int64_t batch, hipStream_t stream);
 }  // namespace dfssm
 
 namespace {
 
 constexpr int64_t kMaxDecodeM = 16;
-constexpr int64_t kGemvMaxK = 8 * 4 * 4 * 128;  // decode kernel's largest K (8 waves x 4 lane groups x 4 chunks)
-// |t| <= 127 * 127 * K must fit int32, and |acc| <= 127 * K with it.
+constexpr int64_t kGemvMaxK = 8 * 4 * 4 * 128;  // decode kernel: 8 waves x 4 lane groups x 4 chunks x 128 k
+// |t| <= 127 * 127 * K must fit int32 (and |acc| <= 127 * K with it)
 constexpr int64_t kMaxK = 131072;
 constexpr int64_t kMaxRows = (int64_t)1 << 31;
+constexpr int64_t kMaxBatch = 65535;  // problems ride gridDim.y
 
+// Operands read with 16-byte vector loads (x, x_q, w_bits, w_a, w_b) must be 16-byte
+// aligned; scale vectors, t, y and acc_dbg only need their element alignment.
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+bool aligned4_or_null(const void* p) { return p == nullptr || aligned4(p); }
 
-bool aligned_or_null(const void* p) { return p == nullptr || aligned16(p); }
+dfssm_status check_rank(int32_t rank) {
+    return (rank == 0 || rank == 16) ? DFSSM_OK : DFSSM_ERR_UNSUPPORTED;
+}
+
+dfssm_status check_sizes(int64_t M, int64_t K, int64_t batch) {
+    if (M <= 0 || K <= 0 || batch <= 0 || M >= kMaxRows) return DFSSM_ERR_INVALID_ARG;
+    if (batch > kMaxBatch) return DFSSM_ERR_UNSUPPORTED;
+    return DFSSM_OK;
+}
+
+dfssm_status lora_down_impl(const int8_t* x_q, int64_t M, int64_t K, const int8_t* w_b, int32_t rank, int32_t* t,
+                            int64_t batch, hipStream_t stream) {
+    if (!x_q || !w_b || !t) return DFSSM_ERR_INVALID_ARG;
+    if (dfssm_status st = check_sizes(M, K, batch)) return st;
+    if (!aligned16(x_q) || !aligned16(w_b) || !aligned4(t)) return DFSSM_ERR_INVALID_ARG;
+    if (rank != 16) return DFSSM_ERR_UNSUPPORTED;
+    if (K > kMaxK) return DFSSM_ERR_UNSUPPORTED;
+    return dfssm::launch_lora_down(x_q, M, K, w_b, t, batch, stream) == hipSuccess ? DFSSM_OK : DFSSM_ERR_HIP;
+}
+
+dfssm_status quantize_lora_down_impl(const float* x, int64_t M, int64_t K, const int8_t* w_b, int32_t rank,
+                                     int8_t* x_q, float* s_x, int32_t* t, int64_t batch, hipStream_t stream) {
+    if (!x || !x_q || !s_x) return DFSSM_ERR_INVALID_ARG;
+    if (dfssm_status st = check_sizes(M, K, batch)) return st;
+    if (!aligned16(x) || !aligned16(x_q) || !aligned4(s_x)) return DFSSM_ERR_INVALID_ARG;
+    if (dfssm_status st = check_rank(rank)) return st;
+    if (rank == 16) {
+        if (!w_b || !t) return DFSSM_ERR_INVALID_ARG;
+        if (!aligned16(w_b) || !aligned4(t)) return DFSSM_ERR_INVALID_ARG;
+        if (K > kMaxK) return DFSSM_ERR_UNSUPPORTED;
+    }
+    if (M * batch >= kMaxRows) return DFSSM_ERR_INVALID_ARG;
+    hipError_t e;
+    if (K % 4 == 0 && dfssm::quantize_lora_tokens_per_group(K) > 0) {
+        e = dfssm::launch_quantize_lora_down(x, M, K, w_b, rank, x_q, s_x, t, batch, stream);
+    } else {
+        // rows not 16-byte aligned, or longer than the fused kernel's LDS holds: two kernels
+        e = dfssm::launch_quantize_act(x, M * batch, K, x_q, s_x, stream);
+        if (e == hipSuccess && rank == 16) e = dfssm::launch_lora_down(x_q, M, K, w_b, t, batch, stream);
+    }
+    return e == hipSuccess ? DFSSM_OK : DFSSM_ERR_HIP;
+}
+
+dfssm_status gemm_impl(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
+                       const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
+                       const float* s_b, const int32_t* t, int32_t rank, float* y, int32_t* acc_dbg, int64_t batch,
+                       hipStream_t stream) {
+    if (!x_q || !s_x || !w_bits || !s_w || !y) return DFSSM_ERR_INVALID_ARG;
+    if (dfssm_status st = check_sizes(M, K, batch)) return st;
+    if (N <= 0 || N >= kMaxRows || (K % 8) != 0) return DFSSM_ERR_INVALID_ARG;
+    if (!aligned16(x_q) || !aligned4(s_x) || !aligned16(w_bits) || !aligned4(s_w) || !aligned4(y) ||
+        !aligned4_or_null(acc_dbg))
+        return DFSSM_ERR_INVALID_ARG;
+    if (dfssm_status st = check_rank(rank)) return st;
+    if (rank == 16) {
+        if (!w_a || !s_a || !s_b || !t) return DFSSM_ERR_INVALID_ARG;
+        if (!aligned16(w_a) || !aligned4(s_a) || !aligned4(s_b) || !aligned4(t)) return DFSSM_ERR_INVALID_ARG;
+    }
+    if (K > kMaxK) return DFSSM_ERR_UNSUPPORTED;
+    hipError_t e;
+    if (M <= kMaxDecodeM && K <= kGemvMaxK) {
+        e = dfssm::launch_gemv(x_q, s_x, (int)M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch,
+                               stream);
+    } else {
+        e = dfssm::launch_gemm_mfma(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch,
+                                    stream);
+    }
+    return e == hipSuccess ? DFSSM_OK : DFSSM_ERR_HIP;
+}
 
 }  // namespace
 
@@ -47,45 +123,50 @@ const char* dfssm_status_string(dfssm_status status) {
     return "DFSSM_ERR_UNKNOWN";
 }
 
-int32_t dfssm_version(void) { return 100; }
+int32_t dfssm_version(void) { return 200; }
 
 dfssm_status dfssm_quantize_act(const float* x, int64_t M, int64_t K, int8_t* x_q, float* s_x,
                                 hipStream_t stream) {
     if (!x || !x_q || !s_x) return DFSSM_ERR_INVALID_ARG;
     if (M <= 0 || K <= 0 || M >= kMaxRows) return DFSSM_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(x_q) || !aligned16(s_x)) return DFSSM_ERR_INVALID_ARG;
-    if (dfssm::launch_quantize_act(x, M, K, x_q, s_x, stream) != hipSuccess) return DFSSM_ERR_HIP;
-    return DFSSM_OK;
+    if (!aligned4(x) || !aligned4(s_x)) return DFSSM_ERR_INVALID_ARG;
+    return dfssm::launch_quantize_act(x, M, K, x_q, s_x, stream) == hipSuccess ? DFSSM_OK : DFSSM_ERR_HIP;
+}
+
+dfssm_status dfssm_lora_down(const int8_t* x_q, int64_t M, int64_t K, const int8_t* w_b, int32_t rank, int32_t* t,
+                             hipStream_t stream) {
+    return lora_down_impl(x_q, M, K, w_b, rank, t, 1, stream);
+}
+
+dfssm_status dfssm_lora_down_strided_batched(const int8_t* x_q, int64_t M, int64_t K, const int8_t* w_b,
+                                             int32_t rank, int32_t* t, int64_t batch, hipStream_t stream) {
+    return lora_down_impl(x_q, M, K, w_b, rank, t, batch, stream);
+}
+
+dfssm_status dfssm_quantize_lora_down(const float* x, int64_t M, int64_t K, const int8_t* w_b, int32_t rank,
+                                      int8_t* x_q, float* s_x, int32_t* t, hipStream_t stream) {
+    return quantize_lora_down_impl(x, M, K, w_b, rank, x_q, s_x, t, 1, stream);
+}
+
+dfssm_status dfssm_quantize_lora_down_strided_batched(const float* x, int64_t M, int64_t K, const int8_t* w_b,
+                                                      int32_t rank, int8_t* x_q, float* s_x, int32_t* t,
+                                                      int64_t batch, hipStream_t stream) {
+    return quantize_lora_down_impl(x, M, K, w_b, rank, x_q, s_x, t, batch, stream);
 }
 
 dfssm_status dfssm_scaffold_lora_gemm(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                                       const uint8_t* w_bits, const float* s_w, const int8_t* w_a,
-                                      const float* s_a, const int8_t* w_b, const float* s_b, int32_t rank,
-                                      float* y, int32_t* t, int32_t* acc_dbg, hipStream_t stream) {
-    if (!x_q || !s_x || !w_bits || !s_w || !y) return DFSSM_ERR_INVALID_ARG;
-    if (M <= 0 || N <= 0 || K <= 0 || (K % 8) != 0) return DFSSM_ERR_INVALID_ARG;
-    if (M >= kMaxRows || N >= kMaxRows) return DFSSM_ERR_INVALID_ARG;
-    if (!aligned16(x_q) || !aligned16(s_x) || !aligned16(w_bits) || !aligned16(s_w) || !aligned16(y) ||
-        !aligned_or_null(acc_dbg))
-        return DFSSM_ERR_INVALID_ARG;
-    if (rank != 0 && rank != 16) return DFSSM_ERR_UNSUPPORTED;
-    if (rank == 16) {
-        if (!w_a || !s_a || !w_b || !s_b || !t) return DFSSM_ERR_INVALID_ARG;
-        if (!aligned16(w_a) || !aligned16(s_a) || !aligned16(w_b) || !aligned16(s_b) || !aligned16(t))
-            return DFSSM_ERR_INVALID_ARG;
-    }
-    if (K > kMaxK) return DFSSM_ERR_UNSUPPORTED;
+                                      const float* s_a, const float* s_b, const int32_t* t, int32_t rank,
+                                      float* y, int32_t* acc_dbg, hipStream_t stream) {
+    return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, 1, stream);
+}
 
-    if (rank == 16) {
-        if (dfssm::launch_lora_down(x_q, M, K, w_b, t, stream) != hipSuccess) return DFSSM_ERR_HIP;
-    }
-    hipError_t e;
-    if (M <= kMaxDecodeM && K <= kGemvMaxK) {
-        e = dfssm::launch_gemv(x_q, s_x, (int)M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, stream);
-    } else {
-        e = dfssm::launch_gemm_mfma(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, stream);
-    }
-    return e == hipSuccess ? DFSSM_OK : DFSSM_ERR_HIP;
+dfssm_status dfssm_scaffold_lora_gemm_strided_batched(const int8_t* x_q, const float* s_x, int64_t M, int64_t N,
+                                                      int64_t K, const uint8_t* w_bits, const float* s_w,
+                                                      const int8_t* w_a, const float* s_a, const float* s_b,
+                                                      const int32_t* t, int32_t rank, float* y, int32_t* acc_dbg,
+                                                      int64_t batch, hipStream_t stream) {
+    return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, stream);
 }
 
 }  // extern "C"

@@ -42,6 +42,23 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     __shared__ float uS[kBM][kRank + 1];
     __shared__ float waS[kBN][kRank + 1];
 
+    // problem blockIdx.y of a dense batch (every operand advanced by its own size)
+    {
+        const int64_t p = blockIdx.y;
+        x_q += p * M * K;
+        s_x += p * M;
+        w_bits += p * N * (K / 8);
+        s_w += p * N;
+        y += p * M * N;
+        if (acc_dbg) acc_dbg += p * M * N;
+        if (rank != 0) {
+            w_a += p * N * kRank;
+            s_a += p * N;
+            s_b += p * kRank;
+            t += p * M * kRank;
+        }
+    }
+
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
@@ -144,16 +161,17 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 hipError_t launch_gemm_mfma(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                             const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
                             const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                            hipStream_t stream) {
+                            int64_t batch, hipStream_t stream) {
     const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
     const int64_t grid = tiles_m * tiles_n;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    const bool fast = (K % 64 == 0);
+    const bool fast = (K % 64 == 0) && ((uintptr_t)x_q % 16 == 0) && ((uintptr_t)w_bits % 16 == 0);
+    const dim3 g3((unsigned)grid, (unsigned)batch);
     if (fast) {
-        gemm_mfma_kernel<true><<<(unsigned)grid, 256, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b,
+        gemm_mfma_kernel<true><<<g3, 256, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b,
                                                                  t, rank, y, acc_dbg, tiles_n);
     } else {
-        gemm_mfma_kernel<false><<<(unsigned)grid, 256, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b,
+        gemm_mfma_kernel<false><<<g3, 256, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b,
                                                                   t, rank, y, acc_dbg, tiles_n);
     }
     return hipGetLastError();

@@ -42,6 +42,23 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     __shared__ int32_t xsum[16];
     __shared__ float u[16][kRank];
 
+    // problem blockIdx.y of a dense batch (every operand advanced by its own size)
+    {
+        const int64_t p = blockIdx.y;
+        x_q += p * M * K;
+        s_x += p * M;
+        w_bits += p * N * (K / 8);
+        s_w += p * N;
+        y += p * M * N;
+        if (acc_dbg) acc_dbg += p * M * N;
+        if (rank != 0) {
+            w_a += p * N * kRank;
+            s_a += p * N;
+            s_b += p * kRank;
+            t += p * M * kRank;
+        }
+    }
+
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int i = lane & 15;
@@ -172,11 +189,14 @@ template <int W, int C>
 static hipError_t launch_gemv_wc(bool fast, const int8_t* x_q, const float* s_x, int M, int64_t N,
                                  int64_t K, const uint8_t* w_bits, const float* s_w, const int8_t* w_a,
                                  const float* s_a, const float* s_b, const int32_t* t, int rank,
-                                 float* y, int32_t* acc_dbg, hipStream_t stream) {
+                                 float* y, int32_t* acc_dbg, int64_t batch, hipStream_t stream) {
+    // Enough workgroups to fill 256 CUs several times over; beyond that each group
+    // takes more row tiles, which amortizes its activation setup.
     const int64_t num_tiles = (N + 15) / 16;
-    const int64_t target_wgs = 512;
-    const int tiles_per_wg = (int)((num_tiles + target_wgs - 1) / target_wgs);
-    const unsigned grid = (unsigned)((num_tiles + tiles_per_wg - 1) / tiles_per_wg);
+    const int64_t target_wgs = 2048;
+    const int64_t per_problem = (target_wgs + batch - 1) / batch;
+    const int tiles_per_wg = (int)((num_tiles + per_problem - 1) / per_problem);
+    const dim3 grid((unsigned)((num_tiles + tiles_per_wg - 1) / tiles_per_wg), (unsigned)batch);
     if (fast) {
         gemv_kernel<W, C, true><<<grid, W * kWave, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b,
                                                                 t, rank, y, acc_dbg, num_tiles, tiles_per_wg);
@@ -191,12 +211,13 @@ static hipError_t launch_gemv_wc(bool fast, const int8_t* x_q, const float* s_x,
 hipError_t launch_gemv(const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
                        const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
                        const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                       hipStream_t stream) {
+                       int64_t batch, hipStream_t stream) {
     const int64_t RB = K / 8;
     const int64_t NC = (RB + 15) / 16;  // 16-byte chunks per row
     const bool fast = (RB % 16 == 0) && ((uintptr_t)w_bits % 16 == 0) && ((uintptr_t)x_q % 16 == 0);
 #define DFSSM_GEMV(Wv, Cv) \
-    return launch_gemv_wc<Wv, Cv>(fast, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, stream)
+    return launch_gemv_wc<Wv, Cv>(fast, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, \
+                                  stream)
     if (NC <= 4) DFSSM_GEMV(1, 1);
     if (NC <= 8) DFSSM_GEMV(2, 1);
     if (NC <= 16) DFSSM_GEMV(4, 1);

@@ -20,6 +20,11 @@ template <bool kFast>
 __global__ __launch_bounds__(kLoraWaves * kWave) void lora_down_kernel(
     const int8_t* __restrict__ x_q, int64_t M, int64_t K, const int8_t* __restrict__ w_b,
     int32_t* __restrict__ t) {
+    // problem blockIdx.y of a dense batch: x_q [M][K], W_B [16][K], t [M][16] each
+    const int64_t p = blockIdx.y;
+    x_q += p * M * K;
+    w_b += p * kRank * K;
+    t += p * M * kRank;
     __shared__ int32_t part[kLoraWaves][16][16];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -55,9 +60,9 @@ __global__ __launch_bounds__(kLoraWaves * kWave) void lora_down_kernel(
 }
 
 hipError_t launch_lora_down(const int8_t* x_q, int64_t M, int64_t K, const int8_t* w_b, int32_t* t,
-                            hipStream_t stream) {
+                            int64_t batch, hipStream_t stream) {
     const bool fast = (K % 16 == 0) && ((uintptr_t)x_q % 16 == 0) && ((uintptr_t)w_b % 16 == 0);
-    const unsigned grid = (unsigned)((M + 15) / 16);
+    const dim3 grid((unsigned)((M + 15) / 16), (unsigned)batch);
     if (fast) {
         lora_down_kernel<true><<<grid, kLoraWaves * kWave, 0, stream>>>(x_q, M, K, w_b, t);
     } else {

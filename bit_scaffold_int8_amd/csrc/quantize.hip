@@ -119,3 +119,147 @@ hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int8_t* x_q
 }
 
 }  // namespace dfssm
+
+// ---------------------------------------------------------------------------------
+// Fused quantizer + LoRA down-projection: one kernel writes x_q, s_x and
+// t[m][r] = sum_k W_B[r][k] x_q[m][k] (technical summary section 2B: the int8 rank-16
+// correction acts on the same int8 activations).  Each workgroup takes up to 16
+// tokens; each wave quantizes whole token rows on its own (wave-level absmax, no
+// block barrier per token, all of a row's loads in flight at once) and also keeps
+// the codes in LDS; then the 16-token x 16-rank tile of t is one
+// v_mfma_i32_16x16x64_i8 accumulator per wave over a K slice, summed through LDS.
+// Requires K % 4 == 0 (16-byte aligned fp32 rows); a group takes as many tokens
+// (at most 16) as fit 63 KiB of LDS, so rows up to 64512 elements.
+namespace dfssm {
+
+constexpr int kQLWaves = 8;
+constexpr int kQLThreads = kQLWaves * kWave;
+constexpr int64_t kQLLdsBytes = 65536 - 1024;  // codes; the rest of 64 KiB holds the t tile
+constexpr int kQLRegVec = 16;  // float4 per lane kept in registers (K <= 4096)
+
+__device__ __forceinline__ float absmax4(float4 v) {
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+__global__ __launch_bounds__(kQLThreads) void quantize_lora_down_kernel(
+    const float* __restrict__ x, int64_t M, int64_t K, const int8_t* __restrict__ w_b, int rank,
+    int8_t* __restrict__ x_q, float* __restrict__ s_x, int32_t* __restrict__ t, int tokens_per_group) {
+    extern __shared__ __align__(16) uint8_t lds_q[];  // [tokens_per_group][K] codes
+    __shared__ int32_t tsum[16][16];                   // t tile [token][rank], summed over waves
+
+    const int64_t p = blockIdx.y;  // problem of a dense batch
+    x += p * M * K;
+    x_q += p * M * K;
+    s_x += p * M;
+    if (rank != 0) {
+        w_b += p * kRank * K;
+        t += p * M * kRank;
+    }
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t m0 = (int64_t)blockIdx.x * tokens_per_group;
+    const int rows = (int)((M - m0) < tokens_per_group ? (M - m0) : tokens_per_group);
+    const int64_t K4 = K / 4;
+    if (threadIdx.x < 256) tsum[threadIdx.x >> 4][threadIdx.x & 15] = 0;
+
+    // ---- phase 1: each wave quantizes rows wave, wave + 8, ...
+    for (int r = wave; r < rows; r += kQLWaves) {
+        const int64_t m = m0 + r;
+        const float4* row4 = reinterpret_cast<const float4*>(x + m * K);
+        uint32_t* q4 = reinterpret_cast<uint32_t*>(x_q + m * K);
+        uint32_t* l4 = reinterpret_cast<uint32_t*>(lds_q + (int64_t)r * K);
+        const bool in_regs = K4 <= (int64_t)kWave * kQLRegVec;
+        float4 v[kQLRegVec];
+        float amax = 0.0f;
+        if (in_regs) {
+#pragma unroll
+            for (int i = 0; i < kQLRegVec; ++i) {
+                const int64_t idx = lane + (int64_t)i * kWave;
+                v[i] = idx < K4 ? row4[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+                amax = fmaxf(amax, absmax4(v[i]));
+            }
+        } else {
+            for (int64_t idx = lane; idx < K4; idx += kWave) amax = fmaxf(amax, absmax4(row4[idx]));
+        }
+        amax = wave_max(amax);
+        const float s = amax / 127.0f;
+        if (lane == 0) s_x[m] = amax == 0.0f ? 0.0f : s;
+        if (in_regs) {
+#pragma unroll
+            for (int i = 0; i < kQLRegVec; ++i) {
+                const int64_t idx = lane + (int64_t)i * kWave;
+                if (idx < K4) {
+                    const uint32_t q = amax == 0.0f ? 0u : quantize4(v[i], s);
+                    q4[idx] = q;
+                    l4[idx] = q;
+                }
+            }
+        } else {
+            for (int64_t idx = lane; idx < K4; idx += kWave) {
+                const uint32_t q = amax == 0.0f ? 0u : quantize4(row4[idx], s);
+                q4[idx] = q;
+                l4[idx] = q;
+            }
+        }
+    }
+    if (rank == 0) return;
+    __syncthreads();
+
+    // ---- phase 2: t tile = codes (16 tokens, LDS) x W_B^T (16 ranks, global)
+    const int i = lane & 15, g = lane >> 4;
+    const uint8_t* arow = lds_q + (int64_t)i * K;
+    const bool arow_live = i < rows;
+    const uint8_t* brow = reinterpret_cast<const uint8_t*>(w_b) + (int64_t)i * K;
+    v4i acc = {0, 0, 0, 0};
+    const int64_t steps = (K + 63) / 64;
+    const bool rows16 = (K % 16) == 0;  // 16-byte aligned rows in LDS and in W_B
+    for (int64_t st = wave; st < steps; st += kQLWaves) {
+        const int64_t off = st * 64 + 16 * g;
+        uint4 a = make_uint4(0u, 0u, 0u, 0u), b = make_uint4(0u, 0u, 0u, 0u);
+        if (rows16 && off + 16 <= K) {
+            if (arow_live) a = *reinterpret_cast<const uint4*>(arow + off);
+            b = *reinterpret_cast<const uint4*>(brow + off);
+        } else if (off < K) {  // rows only 4-byte aligned, or the K tail: word by word
+            uint32_t aw[4] = {0u, 0u, 0u, 0u}, bw[4] = {0u, 0u, 0u, 0u};
+            for (int e = 0; e < 4; ++e) {
+                if (off + 4 * e < K) {
+                    if (arow_live) aw[e] = *reinterpret_cast<const uint32_t*>(arow + off + 4 * e);
+                    bw[e] = *reinterpret_cast<const uint32_t*>(brow + off + 4 * e);
+                }
+            }
+            a = make_uint4(aw[0], aw[1], aw[2], aw[3]);
+            b = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+        }
+        const v4i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+        const v4i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w};
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
+    }
+    // D[4g + v][i] = t[token 4g+v][rank i]; integer adds commute, so LDS atomics
+    // give the exact sum in any order
+#pragma unroll
+    for (int v = 0; v < 4; ++v) atomicAdd(&tsum[4 * g + v][i], acc[v]);
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int tok = threadIdx.x >> 4, r = threadIdx.x & 15;
+        if (tok < rows) t[(m0 + tok) * kRank + r] = tsum[tok][r];
+    }
+}
+
+// Tokens per group so that the codes fit the LDS budget; 0 when one row does not fit.
+int quantize_lora_tokens_per_group(int64_t K) {
+    const int64_t n = kQLLdsBytes / K;
+    return (int)(n >= 16 ? 16 : n);
+}
+
+hipError_t launch_quantize_lora_down(const float* x, int64_t M, int64_t K, const int8_t* w_b, int rank,
+                                     int8_t* x_q, float* s_x, int32_t* t, int64_t batch, hipStream_t stream) {
+    const int tpg = quantize_lora_tokens_per_group(K);
+    if (tpg <= 0 || K % 4 != 0) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((M + tpg - 1) / tpg), (unsigned)batch);
+    const size_t lds = (size_t)tpg * (size_t)K;
+    quantize_lora_down_kernel<<<grid, kQLThreads, lds, stream>>>(x, M, K, w_b, rank, x_q, s_x, t, tpg);
+    return hipGetLastError();
+}
+
+}  // namespace dfssm

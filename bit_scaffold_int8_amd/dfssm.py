@@ -18,7 +18,10 @@ DFSSM_ERR_UNSUPPORTED = 2
 DFSSM_ERR_HIP = 3
 
 # every symbol include/dfssm.h declares
-EXPORTED = ("dfssm_status_string", "dfssm_version", "dfssm_quantize_act", "dfssm_scaffold_lora_gemm")
+EXPORTED = ("dfssm_status_string", "dfssm_version", "dfssm_quantize_act", "dfssm_lora_down",
+            "dfssm_lora_down_strided_batched", "dfssm_quantize_lora_down",
+            "dfssm_quantize_lora_down_strided_batched", "dfssm_scaffold_lora_gemm",
+            "dfssm_scaffold_lora_gemm_strided_batched")
 
 
 class DfssmError(RuntimeError):
@@ -36,10 +39,19 @@ def _load():
     lib.dfssm_status_string.restype = ctypes.c_char_p
     lib.dfssm_version.argtypes = []
     lib.dfssm_version.restype = i32
-    lib.dfssm_quantize_act.argtypes = [P, i64, i64, P, P, P]
-    lib.dfssm_quantize_act.restype = ctypes.c_int
-    lib.dfssm_scaffold_lora_gemm.argtypes = [P, P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P, P]
-    lib.dfssm_scaffold_lora_gemm.restype = ctypes.c_int
+    sigs = {
+        "dfssm_quantize_act": [P, i64, i64, P, P, P],
+        "dfssm_lora_down": [P, i64, i64, P, i32, P, P],
+        "dfssm_lora_down_strided_batched": [P, i64, i64, P, i32, P, i64, P],
+        "dfssm_quantize_lora_down": [P, i64, i64, P, i32, P, P, P, P],
+        "dfssm_quantize_lora_down_strided_batched": [P, i64, i64, P, i32, P, P, P, i64, P],
+        "dfssm_scaffold_lora_gemm": [P, P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P],
+        "dfssm_scaffold_lora_gemm_strided_batched": [P, P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, i64, P],
+    }
+    for name, argtypes in sigs.items():
+        f = getattr(lib, name)
+        f.argtypes = argtypes
+        f.restype = ctypes.c_int
     return lib
 
 
@@ -72,35 +84,68 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def raw_quantize_act(x, M, K, x_q, s_x, stream) -> int:
-    """Pointer-level call; returns the status code unchanged."""
-    return lib.dfssm_quantize_act(x, M, K, x_q, s_x, stream)
+def raw(name: str, *args) -> int:
+    """Pointer-level call of any entry point; returns the status code unchanged."""
+    return getattr(lib, name)(*args)
 
 
-def raw_scaffold_lora_gemm(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, w_b, s_b, rank, y, t, acc_dbg,
-                           stream) -> int:
-    """Pointer-level call; returns the status code unchanged."""
-    return lib.dfssm_scaffold_lora_gemm(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, w_b, s_b, rank,
-                                        y, t, acc_dbg, stream)
+def _call(name, *args):
+    st = getattr(lib, name)(*args)
+    if st != DFSSM_OK:
+        raise DfssmError(st, name)
 
 
 def dfssm_quantize_act(x, x_q, s_x, stream=None) -> None:
-    """x fp32 [M, K] -> x_q int8 [M, K], s_x fp32 [M] (device tensors)."""
+    """x fp32 [M, K] -> x_q int8 [M, K], s_x fp32 [M]."""
     M, K = x.shape
-    st = lib.dfssm_quantize_act(_ptr(x), M, K, _ptr(x_q), _ptr(s_x), _stream(stream))
-    if st != DFSSM_OK:
-        raise DfssmError(st, "dfssm_quantize_act")
+    _call("dfssm_quantize_act", _ptr(x), M, K, _ptr(x_q), _ptr(s_x), _stream(stream))
 
 
-def dfssm_scaffold_lora_gemm(x_q, s_x, w_bits, s_w, w_a, s_a, w_b, s_b, y, t=None, acc_dbg=None,
-                             stream=None) -> None:
-    """y = s_x (s_w (W x_q) + s_A W_A (s_B W_B x_q)); shapes are read from x_q [M, K] and
-    w_bits [N, K/8]; pass w_a = None for rank 0."""
+def dfssm_lora_down(x_q, w_b, t, stream=None) -> None:
+    """t int32 [M, 16] = W_B [16, K] x_q [M, K]^T."""
+    M, K = x_q.shape
+    _call("dfssm_lora_down", _ptr(x_q), M, K, _ptr(w_b), int(w_b.shape[0]), _ptr(t), _stream(stream))
+
+
+def dfssm_lora_down_strided_batched(x_q, w_b, t, stream=None) -> None:
+    """x_q [B, M, K], w_b [B, 16, K] -> t [B, M, 16]."""
+    B, M, K = x_q.shape
+    _call("dfssm_lora_down_strided_batched", _ptr(x_q), M, K, _ptr(w_b), int(w_b.shape[1]), _ptr(t), B,
+          _stream(stream))
+
+
+def dfssm_quantize_lora_down(x, w_b, x_q, s_x, t, stream=None) -> None:
+    """x fp32 [M, K] -> x_q, s_x and (w_b given) t = W_B x_q; w_b = None for rank 0."""
+    M, K = x.shape
+    rank = 0 if w_b is None else int(w_b.shape[0])
+    _call("dfssm_quantize_lora_down", _ptr(x), M, K, _ptr(w_b), rank, _ptr(x_q), _ptr(s_x), _ptr(t),
+          _stream(stream))
+
+
+def dfssm_quantize_lora_down_strided_batched(x, w_b, x_q, s_x, t, stream=None) -> None:
+    """x [B, M, K], w_b [B, 16, K] -> x_q [B, M, K], s_x [B, M], t [B, M, 16]."""
+    B, M, K = x.shape
+    rank = 0 if w_b is None else int(w_b.shape[1])
+    _call("dfssm_quantize_lora_down_strided_batched", _ptr(x), M, K, _ptr(w_b), rank, _ptr(x_q), _ptr(s_x),
+          _ptr(t), B, _stream(stream))
+
+
+def dfssm_scaffold_lora_gemm(x_q, s_x, w_bits, s_w, w_a, s_a, s_b, t, y, acc_dbg=None, stream=None) -> None:
+    """y fp32 [M, N] from x_q [M, K], s_x [M], w_bits [N, K/8], s_w [N] and the LoRA
+    operands w_a [N, 16], s_a [N], s_b [16], t [M, 16] (all None for rank 0)."""
     M, K = x_q.shape
     N = w_bits.shape[0]
-    rank = 0 if w_a is None else int(w_b.shape[0])
-    st = lib.dfssm_scaffold_lora_gemm(_ptr(x_q), _ptr(s_x), M, N, K, _ptr(w_bits), _ptr(s_w),
-                                      _ptr(w_a), _ptr(s_a), _ptr(w_b), _ptr(s_b), rank,
-                                      _ptr(y), _ptr(t), _ptr(acc_dbg), _stream(stream))
-    if st != DFSSM_OK:
-        raise DfssmError(st, "dfssm_scaffold_lora_gemm")
+    rank = 0 if w_a is None else int(w_a.shape[1])
+    _call("dfssm_scaffold_lora_gemm", _ptr(x_q), _ptr(s_x), M, N, K, _ptr(w_bits), _ptr(s_w), _ptr(w_a),
+          _ptr(s_a), _ptr(s_b), _ptr(t), rank, _ptr(y), _ptr(acc_dbg), _stream(stream))
+
+
+def dfssm_scaffold_lora_gemm_strided_batched(x_q, s_x, w_bits, s_w, w_a, s_a, s_b, t, y, acc_dbg=None,
+                                             stream=None) -> None:
+    """Batched form: x_q [B, M, K], s_x [B, M], w_bits [B, N, K/8], s_w [B, N], w_a [B, N, 16],
+    s_a [B, N], s_b [B, 16], t [B, M, 16], y [B, M, N]."""
+    B, M, K = x_q.shape
+    N = w_bits.shape[1]
+    rank = 0 if w_a is None else int(w_a.shape[2])
+    _call("dfssm_scaffold_lora_gemm_strided_batched", _ptr(x_q), _ptr(s_x), M, N, K, _ptr(w_bits), _ptr(s_w),
+          _ptr(w_a), _ptr(s_a), _ptr(s_b), _ptr(t), rank, _ptr(y), _ptr(acc_dbg), B, _stream(stream))

@@ -1,71 +1,96 @@
-"""Device-side plumbing around the C ABI: copy one projection's operands to HBM once,
-preallocate the outputs, and call the two entry points on a stream.
+"""Device-side plumbing around the C ABI: copy projections' operands to HBM once,
+preallocate the outputs, and call the entry points on a stream.
 
 No arithmetic of the projection happens here; it only moves buffers and forwards
-pointers to ``libdfssm.so`` through the ctypes binding.
+pointers to ``libdfssm.so`` through the ctypes binding.  A ``DeviceProjections``
+holds B independent problems of one shape (B = 1 for a single projection) laid
+out densely, as the strided-batched entry points expect.
 """
 from __future__ import annotations
 
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 from . import dfssm
 
 
 @dataclass
-class DeviceProjection:
-    """Resident operands + outputs of one projection (M tokens, K in, N out)."""
-    x: torch.Tensor        # fp32 [M, K]
-    w_bits: torch.Tensor   # uint8 [N, K/8]
-    s_w: torch.Tensor      # fp32 [N]
-    w_a: torch.Tensor | None
-    s_a: torch.Tensor | None
-    w_b: torch.Tensor | None
-    s_b: torch.Tensor | None
-    x_q: torch.Tensor      # int8 [M, K]   (out)
-    s_x: torch.Tensor      # fp32 [M]      (out)
-    y: torch.Tensor        # fp32 [M, N]   (out)
-    t: torch.Tensor | None  # int32 [M, 16] (out)
+class DeviceProjections:
+    x: torch.Tensor         # fp32  [B, M, K]
+    w_bits: torch.Tensor    # uint8 [B, N, K/8]
+    s_w: torch.Tensor       # fp32  [B, N]
+    w_a: torch.Tensor | None   # int8 [B, N, 16]
+    s_a: torch.Tensor | None   # fp32 [B, N]
+    w_b: torch.Tensor | None   # int8 [B, 16, K]
+    s_b: torch.Tensor | None   # fp32 [B, 16]
+    x_q: torch.Tensor       # int8  [B, M, K]   (out)
+    s_x: torch.Tensor       # fp32  [B, M]      (out)
+    t: torch.Tensor | None  # int32 [B, M, 16]  (out)
+    y: torch.Tensor         # fp32  [B, M, N]   (out)
     acc_dbg: torch.Tensor | None
 
     @property
-    def M(self):
+    def B(self):
         return self.x.shape[0]
 
     @property
-    def K(self):
+    def M(self):
         return self.x.shape[1]
 
     @property
+    def K(self):
+        return self.x.shape[2]
+
+    @property
     def N(self):
-        return self.w_bits.shape[0]
+        return self.w_bits.shape[1]
+
+    @property
+    def rank(self):
+        return 0 if self.w_a is None else self.w_a.shape[2]
 
     @classmethod
-    def from_host(cls, x, P, s_w, W_A=None, s_A=None, W_B=None, s_B=None, device="cuda:0",
-                  with_acc: bool = False) -> "DeviceProjection":
-        def dev(a):
-            return None if a is None else torch.from_numpy(a).to(device).contiguous()
-        M, K = x.shape
-        N = P.shape[0]
-        rank = 0 if W_A is None else W_B.shape[0]
+    def from_problems(cls, problems, device="cuda:0", rank: bool = True, with_acc: bool = False):
+        """Stack host problems (objects with x, P, s_w, W_A, s_A, W_B, s_B) onto the device."""
+        def dev(name):
+            return torch.from_numpy(np.stack([getattr(p, name) for p in problems])).to(device).contiguous()
+        B = len(problems)
+        M, K = problems[0].x.shape
+        N = problems[0].P.shape[0]
         return cls(
-            x=dev(x), w_bits=dev(P), s_w=dev(s_w), w_a=dev(W_A), s_a=dev(s_A), w_b=dev(W_B), s_b=dev(s_B),
-            x_q=torch.empty((M, K), dtype=torch.int8, device=device),
-            s_x=torch.empty((M,), dtype=torch.float32, device=device),
-            y=torch.empty((M, N), dtype=torch.float32, device=device),
-            t=torch.empty((M, rank), dtype=torch.int32, device=device) if rank else None,
-            acc_dbg=torch.empty((M, N), dtype=torch.int32, device=device) if with_acc else None,
+            x=dev("x"), w_bits=dev("P"), s_w=dev("s_w"),
+            w_a=dev("W_A") if rank else None, s_a=dev("s_A") if rank else None,
+            w_b=dev("W_B") if rank else None, s_b=dev("s_B") if rank else None,
+            x_q=torch.empty((B, M, K), dtype=torch.int8, device=device),
+            s_x=torch.empty((B, M), dtype=torch.float32, device=device),
+            t=torch.empty((B, M, 16), dtype=torch.int32, device=device) if rank else None,
+            y=torch.empty((B, M, N), dtype=torch.float32, device=device),
+            acc_dbg=torch.empty((B, M, N), dtype=torch.int32, device=device) if with_acc else None,
         )
 
-    def quantize(self, stream=None):
-        dfssm.dfssm_quantize_act(self.x, self.x_q, self.s_x, stream)
+    # ---- the two launches of a forward step
+    def quantize_lora_down(self, stream=None):
+        dfssm.dfssm_quantize_lora_down_strided_batched(self.x, self.w_b, self.x_q, self.s_x, self.t, stream)
 
     def gemm(self, stream=None, debug: bool = True):
-        dfssm.dfssm_scaffold_lora_gemm(self.x_q, self.s_x, self.w_bits, self.s_w, self.w_a, self.s_a,
-                                       self.w_b, self.s_b, self.y, self.t,
-                                       self.acc_dbg if debug else None, stream)
+        dfssm.dfssm_scaffold_lora_gemm_strided_batched(
+            self.x_q, self.s_x, self.w_bits, self.s_w, self.w_a, self.s_a, self.s_b, self.t, self.y,
+            self.acc_dbg if debug else None, stream)
 
     def forward(self, stream=None, debug: bool = True):
-        self.quantize(stream)
+        self.quantize_lora_down(stream)
         self.gemm(stream, debug)
+
+    # ---- the unfused entry points, problem by problem (single-problem API)
+    def forward_unfused(self, stream=None, debug: bool = True):
+        for b in range(self.B):
+            dfssm.dfssm_quantize_act(self.x[b], self.x_q[b], self.s_x[b], stream)
+            if self.rank:
+                dfssm.dfssm_lora_down(self.x_q[b], self.w_b[b], self.t[b], stream)
+            dfssm.dfssm_scaffold_lora_gemm(
+                self.x_q[b], self.s_x[b], self.w_bits[b], self.s_w[b],
+                None if not self.rank else self.w_a[b], None if not self.rank else self.s_a[b],
+                None if not self.rank else self.s_b[b], None if not self.rank else self.t[b], self.y[b],
+                None if (self.acc_dbg is None or not debug) else self.acc_dbg[b], stream)

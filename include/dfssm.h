@@ -16,7 +16,12 @@
  *   y[m][n]   = s_x[m] * ( s_w[n] * acc[m][n]
  *                          + s_A[n] * sum_r W_A[n][r] * s_B[r] * t[m][r] )   (fp32)
  *
- * Data layout (all row-major, contiguous, device memory unless stated):
+ * A forward step is two calls: dfssm_quantize_lora_down (x -> x_q, s_x, t) and
+ * dfssm_scaffold_lora_gemm (x_q, s_x, t -> y).  The LoRA down-projection t is a
+ * reduction over all of K that every output needs, so it is produced before the
+ * main kernel, which then runs without any cross-workgroup dependency.
+ *
+ * Data layout (all row-major, contiguous, device memory):
  *   x      fp32  [M][K]
  *   x_q    int8  [M][K]          s_x  fp32 [M]
  *   w_bits uint8 [N][K/8]        bit b of byte j of row n is the sign of w[n][8j+b]:
@@ -24,20 +29,30 @@
  *   s_w    fp32  [N]             per-output-channel scaffold scale
  *   w_a    int8  [N][rank]       s_a fp32 [N]      (LoRA up, per-row scale)
  *   w_b    int8  [rank][K]       s_b fp32 [rank]   (LoRA down, per-row scale)
- *   t      int32 [M][rank]       LoRA down-projection (written by the library)
+ *   t      int32 [M][rank]       LoRA down-projection
  *   y      fp32  [M][N]
+ * Alignment: x_q, w_bits, w_a, w_b (and x, except in dfssm_quantize_act) must be
+ * 16-byte aligned; s_x, s_w, s_a, s_b, t, y, acc_dbg need 4-byte alignment.
+ * Allocator-returned buffers satisfy both.
  *
  * Ownership and threading: the caller owns every buffer; the library keeps
- * pointers only for the duration of a call, allocates no device memory on
- * these entry points, never synchronizes the stream, and enqueues all work on
- * `stream` (0 = the default stream), so the calls may be captured in a HIP
- * graph.  Calls on different streams are independent as long as their output
- * buffers do not overlap.
+ * pointers only for the duration of a call, allocates no memory, never
+ * synchronizes the stream, and enqueues all work on `stream` (0 = the default
+ * stream), so calls may be captured in a HIP graph.  Calls on different streams
+ * are independent as long as their output buffers do not overlap.
  *
- * Errors: arguments are validated on the host before anything is enqueued; on
- * a validation error nothing is launched.  DFSSM_ERR_HIP reports a launch
- * failure (hipGetLastError after the launch).  Non-finite x is a documented
- * precondition violation: results are then unspecified.
+ * Errors: arguments are validated on the host before anything is enqueued; on a
+ * validation error nothing is launched.  DFSSM_ERR_HIP reports a launch failure
+ * (hipGetLastError after the launch).  Non-finite x is a documented precondition
+ * violation: results are then unspecified.
+ *
+ * Batched forms: `batch` independent problems of identical shape in one launch
+ * (each layer's projection has its own scaffold and LoRA pair; independent
+ * inputs -- rotated weight copies, layers fed independent activations -- can
+ * share the launch cost).  Operands of problem p follow those of problem p-1
+ * densely in every buffer: x + p*M*K, x_q + p*M*K, s_x + p*M, w_bits + p*N*K/8,
+ * s_w + p*N, w_a + p*N*16, s_a + p*N, w_b + p*16*K, s_b + p*16, t + p*M*16,
+ * y + p*M*N, acc_dbg + p*M*N.  1 <= batch <= 65535.
  */
 #ifndef DFSSM_H
 #define DFSSM_H
@@ -52,21 +67,21 @@ extern "C" {
 
 typedef enum {
     DFSSM_OK = 0,
-    DFSSM_ERR_INVALID_ARG = 1,   /* NULL required pointer, M/N/K <= 0, K % 8 != 0, misaligned pointer */
-    DFSSM_ERR_UNSUPPORTED = 2,   /* rank other than 0 or 16 */
+    DFSSM_ERR_INVALID_ARG = 1,   /* NULL required pointer, size <= 0, K % 8 != 0 (gemm), misaligned pointer */
+    DFSSM_ERR_UNSUPPORTED = 2,   /* rank other than 0 or 16, K > 131072, batch > 65535 */
     DFSSM_ERR_HIP = 3            /* the HIP runtime reported an error for a launch */
 } dfssm_status;
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* dfssm_status_string(dfssm_status status);
 
-/* Library version as major*10000 + minor*100 + patch. */
+/* Library version as major*100 + minor. */
 int32_t dfssm_version(void);
 
 /*
- * Per-token absmax int8 quantization of activations (the int8 operand of the
- * scaffold product; technical summary section 2C).
- *   x    fp32 [M][K], read only, 4-byte aligned
+ * Per-token absmax int8 quantization of activations, the int8 operand of the
+ * scaffold product (technical summary section 2C).
+ *   x    fp32 [M][K], read
  *   x_q  int8 [M][K], written
  *   s_x  fp32 [M],    written (0 for an all-zero token, whose codes are all 0)
  * Requires M >= 1, K >= 1.  Bit-exact with the IEEE definition above.
@@ -75,28 +90,56 @@ dfssm_status dfssm_quantize_act(const float* x, int64_t M, int64_t K,
                                 int8_t* x_q, float* s_x, hipStream_t stream);
 
 /*
- * Scaffold + LoRA projection y = s_x . (s_w . (W x_q) + s_A . W_A (s_B . W_B x_q))
- * (technical summary sections 2B and 2C).
- *   x_q, s_x     the quantized activations (as written by dfssm_quantize_act)
+ * LoRA down-projection t = W_B x_q in exact int32 (technical summary section 2B).
+ *   x_q int8 [M][K], w_b int8 [rank][K], t int32 [M][rank] (written).
+ * rank must be 16 (DFSSM_ERR_UNSUPPORTED otherwise); K <= 131072 keeps
+ * |t| <= 127*127*K within int32.
+ */
+dfssm_status dfssm_lora_down(const int8_t* x_q, int64_t M, int64_t K, const int8_t* w_b, int32_t rank,
+                             int32_t* t, hipStream_t stream);
+dfssm_status dfssm_lora_down_strided_batched(const int8_t* x_q, int64_t M, int64_t K, const int8_t* w_b,
+                                             int32_t rank, int32_t* t, int64_t batch, hipStream_t stream);
+
+/*
+ * dfssm_quantize_act and dfssm_lora_down fused into one kernel: writes x_q, s_x and
+ * (rank 16) t.  With rank 0, w_b and t may be NULL and only x_q, s_x are written.
+ * Results are identical to the two separate calls.
+ */
+dfssm_status dfssm_quantize_lora_down(const float* x, int64_t M, int64_t K, const int8_t* w_b, int32_t rank,
+                                      int8_t* x_q, float* s_x, int32_t* t, hipStream_t stream);
+dfssm_status dfssm_quantize_lora_down_strided_batched(const float* x, int64_t M, int64_t K,
+                                                      const int8_t* w_b, int32_t rank, int8_t* x_q,
+                                                      float* s_x, int32_t* t, int64_t batch,
+                                                      hipStream_t stream);
+
+/*
+ * Scaffold product with the fused scale + LoRA-up epilogue (technical summary
+ * sections 2B and 2C): y = s_x . (s_w . (W x_q) + s_A . W_A (s_B . t)).
+ *   x_q, s_x     quantized activations (dfssm_quantize_act)
  *   w_bits, s_w  the 1-bit scaffold and its per-output-channel scale
- *   w_a, s_a, w_b, s_b, rank   the int8 LoRA pair; rank must be 16, or 0 for no
- *                correction (then w_a, s_a, w_b, s_b may be NULL)
+ *   w_a, s_a, s_b, t, rank  the LoRA up factor, its scales and t = W_B x_q
+ *                (dfssm_lora_down); rank 16, or 0 for no correction (then
+ *                w_a, s_a, s_b, t may be NULL)
  *   y            fp32 [M][N], written
- *   t            int32 [M][rank], written when rank == 16 (may be NULL when
- *                rank == 0); it carries W_B x_q from the LoRA-down kernel to
- *                the epilogue, and its values are exact
  *   acc_dbg      optional int32 [M][N]: when not NULL, also receives the exact
- *                scaffold accumulators sum_k w x_q (for verification; slower)
- * Requires M, N >= 1, K >= 8, K % 8 == 0, w_bits 4-byte aligned.
- * M <= 16 runs the bandwidth-bound decode kernel; larger M the int8 MFMA kernel.
+ *                scaffold accumulators sum_k w x_q (verification aid)
+ * Requires M, N >= 1, K >= 8, K % 8 == 0, K <= 131072.  M <= 16 (with K <= 16384)
+ * runs the bandwidth-bound decode kernel, otherwise the int8 MFMA kernel; either
+ * way one kernel launch.
  */
 dfssm_status dfssm_scaffold_lora_gemm(const int8_t* x_q, const float* s_x,
                                       int64_t M, int64_t N, int64_t K,
                                       const uint8_t* w_bits, const float* s_w,
-                                      const int8_t* w_a, const float* s_a,
-                                      const int8_t* w_b, const float* s_b, int32_t rank,
-                                      float* y, int32_t* t, int32_t* acc_dbg,
-                                      hipStream_t stream);
+                                      const int8_t* w_a, const float* s_a, const float* s_b,
+                                      const int32_t* t, int32_t rank,
+                                      float* y, int32_t* acc_dbg, hipStream_t stream);
+dfssm_status dfssm_scaffold_lora_gemm_strided_batched(const int8_t* x_q, const float* s_x,
+                                                      int64_t M, int64_t N, int64_t K,
+                                                      const uint8_t* w_bits, const float* s_w,
+                                                      const int8_t* w_a, const float* s_a, const float* s_b,
+                                                      const int32_t* t, int32_t rank,
+                                                      float* y, int32_t* acc_dbg,
+                                                      int64_t batch, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -43,6 +43,11 @@ def test_status_strings_and_version():
 A = 0x10000
 
 
+def _raw(name, *args):
+    from bit_scaffold_int8_amd import dfssm
+    return dfssm.raw(name, *args)
+
+
 @pytest.mark.parametrize("args,want", [
     ((None, 1, 8, A, A), 1),           # NULL x
     ((A, 1, 8, None, A), 1),           # NULL x_q
@@ -50,31 +55,64 @@ A = 0x10000
     ((A, 0, 8, A, A), 1),              # M = 0
     ((A, 1, 0, A, A), 1),              # K = 0
     ((A, -3, 8, A, A), 1),             # M < 0
-    ((A + 4, 1, 8, A, A), 1),          # misaligned x
-    ((A, 1, 8, A + 1, A), 1),          # misaligned x_q
+    ((A + 2, 1, 8, A, A), 1),          # x not float-aligned
+    ((A, 1, 8, A, A + 1), 1),          # s_x not float-aligned
 ])
 def test_quantize_rejects(args, want):
-    from bit_scaffold_int8_amd import dfssm
     x, M, K, x_q, s_x = args
-    assert dfssm.raw_quantize_act(x, M, K, x_q, s_x, None) == want
+    assert _raw("dfssm_quantize_act", x, M, K, x_q, s_x, None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x_q=None), 1), (dict(w_b=None), 1), (dict(t=None), 1), (dict(M=0), 1), (dict(K=0), 1),
+    (dict(x_q=A + 4), 1), (dict(w_b=A + 8), 1), (dict(t=A + 2), 1),
+    (dict(rank=0), 2), (dict(rank=8), 2), (dict(K=131072 + 16), 2), (dict(batch=0), 1), (dict(batch=70000), 2),
+])
+def test_lora_down_rejects(kw, want):
+    a = dict(x_q=A, M=1, K=64, w_b=A, rank=16, t=A, batch=1)
+    a.update(kw)
+    assert _raw("dfssm_lora_down_strided_batched", a["x_q"], a["M"], a["K"], a["w_b"], a["rank"], a["t"],
+                a["batch"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), 1), (dict(x_q=None), 1), (dict(s_x=None), 1), (dict(M=0), 1), (dict(K=0), 1),
+    (dict(x=A + 4), 1), (dict(x_q=A + 4), 1), (dict(s_x=A + 2), 1),
+    (dict(w_b=None), 1), (dict(t=None), 1), (dict(w_b=A + 8), 1), (dict(t=A + 1), 1),
+    (dict(rank=4), 2), (dict(batch=0), 1), (dict(batch=65536), 2),
+])
+def test_quantize_lora_down_rejects(kw, want):
+    a = dict(x=A, M=1, K=64, w_b=A, rank=16, x_q=A, s_x=A, t=A, batch=1)
+    a.update(kw)
+    assert _raw("dfssm_quantize_lora_down_strided_batched", a["x"], a["M"], a["K"], a["w_b"], a["rank"],
+                a["x_q"], a["s_x"], a["t"], a["batch"], None) == want
 
 
 def _gemm(**kw):
-    from bit_scaffold_int8_amd import dfssm
-    a = dict(x_q=A, s_x=A, M=1, N=16, K=64, w_bits=A, s_w=A, w_a=A, s_a=A, w_b=A, s_b=A, rank=16,
-             y=A, t=A, acc_dbg=None, stream=None)
+    a = dict(x_q=A, s_x=A, M=1, N=16, K=64, w_bits=A, s_w=A, w_a=A, s_a=A, s_b=A, t=A, rank=16,
+             y=A, acc_dbg=None, batch=1)
     a.update(kw)
-    return dfssm.raw_scaffold_lora_gemm(**a)
+    return _raw("dfssm_scaffold_lora_gemm_strided_batched", a["x_q"], a["s_x"], a["M"], a["N"], a["K"],
+                a["w_bits"], a["s_w"], a["w_a"], a["s_a"], a["s_b"], a["t"], a["rank"], a["y"], a["acc_dbg"],
+                a["batch"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
     (dict(x_q=None), 1), (dict(s_x=None), 1), (dict(w_bits=None), 1), (dict(s_w=None), 1),
     (dict(y=None), 1),
-    (dict(M=0), 1), (dict(N=0), 1), (dict(K=0), 1), (dict(K=12), 1), (dict(K=-8), 1),
-    (dict(w_a=None), 1), (dict(s_a=None), 1), (dict(w_b=None), 1), (dict(s_b=None), 1), (dict(t=None), 1),
-    (dict(w_bits=A + 8), 1), (dict(y=A + 4), 1), (dict(acc_dbg=A + 2), 1), (dict(t=A + 4), 1),
+    (dict(M=0), 1), (dict(N=0), 1), (dict(K=0), 1), (dict(K=12), 1), (dict(K=-8), 1), (dict(batch=0), 1),
+    (dict(w_a=None), 1), (dict(s_a=None), 1), (dict(s_b=None), 1), (dict(t=None), 1),
+    (dict(w_bits=A + 8), 1), (dict(x_q=A + 4), 1), (dict(w_a=A + 4), 1), (dict(y=A + 2), 1),
+    (dict(acc_dbg=A + 2), 1), (dict(t=A + 1), 1), (dict(s_w=A + 1), 1),
     (dict(rank=8), 2), (dict(rank=32), 2), (dict(rank=-1), 2),
-    (dict(K=131072 + 8), 2),
+    (dict(K=131072 + 8), 2), (dict(batch=65536), 2),
 ])
 def test_gemm_rejects(kw, want):
     assert _gemm(**kw) == want
+
+
+def test_single_problem_gemm_rejects_like_batched():
+    assert _raw("dfssm_scaffold_lora_gemm", A, A, 1, 16, 12, A, A, A, A, A, A, 16, A, None, None) == 1
+    assert _raw("dfssm_scaffold_lora_gemm", A, A, 1, 16, 64, A, A, A, A, A, A, 8, A, None, None) == 2
+    assert _raw("dfssm_lora_down", A, 1, 64, A, 0, A, None) == 2
+    assert _raw("dfssm_quantize_lora_down", A, 1, 64, None, 16, A, A, A, None) == 1

@@ -25,21 +25,22 @@ def torch_cuda():
     return torch
 
 
-def _run_hip(prob, with_acc=True, rank=16):
-    from bit_scaffold_int8_amd.runner import DeviceProjection
+def _run_hip(prob, with_acc=True, rank=16, path="fused"):
+    """Run one problem through the C ABI; path 'fused' = quantize_lora_down + gemm
+    (batched entry points, batch 1), 'unfused' = quantize_act, lora_down, gemm."""
+    from bit_scaffold_int8_amd.runner import DeviceProjections
     import torch
-    if rank:
-        dp = DeviceProjection.from_host(prob.x, prob.P, prob.s_w, prob.W_A, prob.s_A, prob.W_B, prob.s_B,
-                                        with_acc=with_acc)
+    dp = DeviceProjections.from_problems([prob], rank=bool(rank), with_acc=with_acc)
+    if path == "fused":
+        dp.forward()
     else:
-        dp = DeviceProjection.from_host(prob.x, prob.P, prob.s_w, with_acc=with_acc)
-    dp.forward()
+        dp.forward_unfused()
     torch.cuda.synchronize()
-    out = dict(x_q=dp.x_q.cpu().numpy(), s_x=dp.s_x.cpu().numpy(), y=dp.y.cpu().numpy())
+    out = dict(x_q=dp.x_q[0].cpu().numpy(), s_x=dp.s_x[0].cpu().numpy(), y=dp.y[0].cpu().numpy())
     if rank:
-        out["t"] = dp.t.cpu().numpy()
+        out["t"] = dp.t[0].cpu().numpy()
     if with_acc:
-        out["acc"] = dp.acc_dbg.cpu().numpy()
+        out["acc"] = dp.acc_dbg[0].cpu().numpy()
     return out
 
 
@@ -60,8 +61,8 @@ def _assert_y(y, y_ref, D, where=""):
                            f"worst err/D = {(err / np.maximum(D, 1e-300)).max():.3e}")
 
 
-def _check_full(prob, rank=16, nthreads=8):
-    got = _run_hip(prob, rank=rank)
+def _check_full(prob, rank=16, nthreads=8, path="fused"):
+    got = _run_hip(prob, rank=rank, path=path)
     xq_ref, sx_ref = oracle.quantize_act(prob.x)
     assert np.array_equal(got["s_x"].view(np.uint32), sx_ref.view(np.uint32)), "s_x not bit-exact"
     assert np.array_equal(got["x_q"], xq_ref), "x_q not bit-exact"
@@ -161,6 +162,69 @@ def test_ragged_shapes(torch_cuda, M, N, K):
 @pytest.mark.parametrize("M", [1, 5, 40])
 def test_rank_zero(torch_cuda, M):
     _check_full(si.make_problem(M, 96, 1024, 2, seed=77 + M), rank=0)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 2048, 4096), (4, 300, 2048), (16, 64, 1000), (40, 90, 520),
+                                   (2, 70, 72), (1, 33, 65536)])
+def test_unfused_entry_points(torch_cuda, M, N, K):
+    # quantize_act, lora_down and gemm called one by one
+    _check_full(si.make_problem(M, N, K, 2, seed=5 * M + K), path="unfused")
+
+
+@pytest.mark.parametrize("M,K", [(1, 65536), (3, 65544), (2, 131072)])
+def test_long_rows_take_the_two_kernel_fallback(torch_cuda, M, K):
+    # rows too long for the fused kernel's LDS: quantize + lora_down run as two kernels
+    _check_full(si.make_problem(M, 24, K, 2, seed=K + M))
+
+
+@pytest.mark.parametrize("M,K", [(1, 1), (3, 7), (2, 1001), (5, 4099)])
+def test_quantize_act_any_row_length(torch_cuda, M, K):
+    import torch
+    from bit_scaffold_int8_amd import dfssm
+    rng = np.random.default_rng(M * 100 + K)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    x[0, 0] = 30.0
+    xd = torch.from_numpy(x).cuda()
+    x_q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    s_x = torch.empty((M,), dtype=torch.float32, device="cuda")
+    dfssm.dfssm_quantize_act(xd, x_q, s_x)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_act(x)
+    assert np.array_equal(x_q.cpu().numpy(), q_ref)
+    assert np.array_equal(s_x.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("B,M,N,K", [(5, 1, 2048, 4096), (3, 4, 8512, 2048), (4, 33, 100, 1024), (7, 2, 40, 136)])
+def test_strided_batched_matches_oracle_per_problem(torch_cuda, B, M, N, K):
+    import torch
+    from bit_scaffold_int8_amd.runner import DeviceProjections
+    probs = si.make_copies(M, N, K, 2, seed=B * 1000 + K, copies=B)
+    dp = DeviceProjections.from_problems(probs, with_acc=True)
+    dp.forward()
+    torch.cuda.synchronize()
+    for b, prob in enumerate(probs):
+        xq_ref, sx_ref = oracle.quantize_act(prob.x)
+        y_ref, acc_ref, t_ref = oracle.scaffold_lora_gemm(xq_ref, sx_ref, prob.P, prob.s_w, prob.W_A, prob.s_A,
+                                                          prob.W_B, prob.s_B, nthreads=8)
+        assert np.array_equal(dp.x_q[b].cpu().numpy(), xq_ref)
+        assert np.array_equal(dp.t[b].cpu().numpy(), t_ref)
+        assert np.array_equal(dp.acc_dbg[b].cpu().numpy(), acc_ref)
+        D = _magnitude(sx_ref, prob.s_w, acc_ref, prob.s_A, prob.W_A, prob.s_B, t_ref)
+        _assert_y(dp.y[b].cpu().numpy(), y_ref, D, f"batch {b}")
+
+
+def test_gemm_without_debug_output_gives_same_y(torch_cuda):
+    import torch
+    from bit_scaffold_int8_amd.runner import DeviceProjections
+    for (M, N, K) in [(1, 2048, 4096), (300, 200, 512)]:
+        dp = DeviceProjections.from_problems([si.make_problem(M, N, K, 2, seed=3)], with_acc=True)
+        dp.forward(debug=True)
+        torch.cuda.synchronize()
+        y1 = dp.y.clone()
+        dp.y.zero_()
+        dp.forward(debug=False)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, dp.y)
 
 
 def test_zero_token_and_exact_ties(torch_cuda):
