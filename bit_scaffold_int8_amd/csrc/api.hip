@@ -99,7 +99,9 @@ dfssm_status gemm_impl(const int8_t* x_q, const float* s_x, int64_t M, int64_t N
     }
     if (K > kMaxK) return DFSSM_ERR_UNSUPPORTED;
     hipError_t e;
-    if (M <= kMaxDecodeM && K <= kGemvMaxK) {
+    // the decode kernel addresses one problem's signs and outputs with 32-bit offsets
+    const bool gemv_fits = N * (K / 8) < ((int64_t)1 << 31) && M * N * 4 < ((int64_t)1 << 31);
+    if (M <= kMaxDecodeM && K <= kGemvMaxK && gemv_fits) {
         e = dfssm::launch_gemv(x_q, s_x, (int)M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch,
                                stream);
     } else {

@@ -40,31 +40,92 @@ __device__ __forceinline__ int32_t byte_sum(uint32_t w, int32_t acc) {
 }
 
 // 16-byte load of bytes [off, off+16) of a buffer of `limit` bytes; bytes past the
-// limit read as zero.  `fast` promises 16-byte alignment of base+off whenever the
-// whole chunk is in range.
-__device__ __forceinline__ uint4 load16_guarded(const uint8_t* base, int64_t off, int64_t limit,
-                                                bool fast) {
-    if (off + 16 <= limit && fast) {
-        return *reinterpret_cast<const uint4*>(base + off);
+// limit read as zero.  kFast: the caller guarantees base+off is 16-byte aligned and
+// limit a multiple of 16, so a chunk is either wholly inside or wholly outside and a
+// single masked vector load suffices.  Otherwise bytes are gathered one by one.
+template <bool kFast>
+__device__ __forceinline__ uint4 load16_guarded(const uint8_t* base, int64_t off, int64_t limit) {
+    if constexpr (kFast) {
+        return off < limit ? *reinterpret_cast<const uint4*>(base + off) : make_uint4(0u, 0u, 0u, 0u);
+    } else {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int b = 0; b < 16; ++b) {
+            if (off + b < limit) w[b >> 2] |= uint32_t(base[off + b]) << (8 * (b & 3));
+        }
+        return make_uint4(w[0], w[1], w[2], w[3]);
     }
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    for (int b = 0; b < 16; ++b) {
-        if (off + b < limit) w[b >> 2] |= uint32_t(base[off + b]) << (8 * (b & 3));
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// 4-byte load of bytes [off, off+4) with the same zero-fill rule.
-__device__ __forceinline__ uint32_t load4_guarded(const uint8_t* base, int64_t off, int64_t limit,
-                                                  bool fast) {
-    if (off + 4 <= limit && fast) {
-        return *reinterpret_cast<const uint32_t*>(base + off);
+// 4-byte load of bytes [off, off+4) with the same rule (kFast: 4-byte aligned, limit
+// a multiple of 4).
+template <bool kFast>
+__device__ __forceinline__ uint32_t load4_guarded(const uint8_t* base, int64_t off, int64_t limit) {
+    if constexpr (kFast) {
+        return off < limit ? *reinterpret_cast<const uint32_t*>(base + off) : 0u;
+    } else {
+        uint32_t w = 0u;
+        for (int b = 0; b < 4; ++b) {
+            if (off + b < limit) w |= uint32_t(base[off + b]) << (8 * b);
+        }
+        return w;
     }
-    uint32_t w = 0u;
-    for (int b = 0; b < 4; ++b) {
-        if (off + b < limit) w |= uint32_t(base[off + b]) << (8 * b);
-    }
-    return w;
+}
+
+// 16-byte load that never branches: `base` must point at 16 readable bytes; the
+// value is returned when `live`, zero otherwise (dead lanes read base itself).
+// The zeroing is an AND with a mask the optimizer cannot see through (an empty asm
+// statement with a register operand emits no instruction); a plain select lets it
+// sink the load into a branch, which costs a wait per load.
+__device__ __forceinline__ uint32_t opaque_mask(bool live) {
+    uint32_t m = live ? 0xFFFFFFFFu : 0u;
+    asm volatile("" : "+v"(m));
+    return m;
+}
+
+__device__ __forceinline__ uint4 load16_select(const uint8_t* base, int64_t off, bool live) {
+    const uint4 v = *reinterpret_cast<const uint4*>(base + (live ? off : 0));
+    const uint32_t m = opaque_mask(live);
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also orders
+// global memory, which makes every wave wait for all of its outstanding global
+// loads (s_waitcnt vmcnt(0)) and so drains a software prefetch pipeline; this one
+// lets prefetched loads stay in flight across the barrier.  Only for barriers that
+// publish LDS data, never for global-memory hand-offs between threads.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Raw buffer resource over [base, base + bytes).  A buffer access past `bytes` is
+// dropped (store) or reads zero (load) by the hardware range check, so an offset of
+// kOffDead predicates a store without a branch -- and without the control flow that
+// makes the compiler wait for every outstanding load at the join.  Word 3 is the
+// gfx9-family raw-buffer default.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+constexpr int kOffDead = 0x7fffffff;
+
+__device__ __forceinline__ void store_f32(float v, __amdgpu_buffer_rsrc_t r, int byte_off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, 0);
+}
+
+__device__ __forceinline__ void store_i32(int32_t v, __amdgpu_buffer_rsrc_t r, int byte_off) {
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, r, byte_off, 0, 0);
+}
+
+// A shift amount of 1 the optimizer cannot see (an empty asm statement with a scalar
+// register operand emits no instruction).  With a constant shift, InstCombine
+// re-associates a Horner chain (((a << 1) + b) << 1) + c into separate shifts and
+// adds; with this one every step stays a single v_lshl_add_u32.  No instruction is
+// written by hand, so the compiler still inserts the MFMA-to-VALU wait states.
+__device__ __forceinline__ int32_t opaque_one() {
+    int32_t one = 1;
+    asm volatile("" : "+s"(one));
+    return one;
 }
 
 __device__ __forceinline__ float wave_max(float v) {

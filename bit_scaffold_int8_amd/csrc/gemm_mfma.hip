@@ -92,11 +92,11 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         for (int b = 0; b < 2; ++b) acc[a][b] = (v16i){};
 
     for (int64_t k0 = 0; k0 < K; k0 += kBK) {
-        const uint4 a0 = load16_guarded(xrow, k0 + 32 * shalf, xlimit, kFast);
-        const uint4 a1 = load16_guarded(xrow, k0 + 32 * shalf + 16, xlimit, kFast);
+        const uint4 a0 = load16_guarded<kFast>(xrow, k0 + 32 * shalf, xlimit);
+        const uint4 a1 = load16_guarded<kFast>(xrow, k0 + 32 * shalf + 16, xlimit);
         uint32_t bw[2];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) bw[nb] = load4_guarded(brow[nb], k0 / 8 + 4 * g, blimit[nb], kFast);
+        for (int nb = 0; nb < 2; ++nb) bw[nb] = load4_guarded<kFast>(brow[nb], k0 / 8 + 4 * g, blimit[nb]);
         rs = byte_sum(a0.x, rs); rs = byte_sum(a0.y, rs); rs = byte_sum(a0.z, rs); rs = byte_sum(a0.w, rs);
         rs = byte_sum(a1.x, rs); rs = byte_sum(a1.y, rs); rs = byte_sum(a1.z, rs); rs = byte_sum(a1.w, rs);
         __syncthreads();  // previous K-step's fragment reads are done

@@ -11,10 +11,10 @@
 //    headroom over the packed-bit stream, so M = 1, 4 and 16 cost the same ALU work.
 //  * Bit-plane expansion: a 32-bit word of packed signs covers k = 8b + j (byte b,
 //    bit j).  AND with (0x01010101 << j) yields four bytes 2^j * bit for k = j, j+8,
-//    j+16, j+24 -- one VALU op per four expanded weights, half the cost of any
-//    in-order expansion.  Each plane j feeds its own accumulator; the planes are
-//    recombined exactly at the end (acc_j is a multiple of 2^j; plane 7 reads as
-//    -128 in signed int8 and is negated).
+//    j+16, j+24 -- one VALU op per four expanded weights.  Planes 4..7 come from the
+//    word shifted right by 4 under the same four masks, so planes j and j+4 share
+//    accumulator j (weights 2^j, never the int8 sign bit); the four accumulators are
+//    recombined exactly once per tile as (8 acc0 + 4 acc1 + 2 acc2 + acc3) / 8.
 //  * The activations are permuted once per workgroup into the same plane order
 //    (byte transposes with v_perm_b32) and stay in VGPRs for every row tile.
 //  * 0/1 weights give S = sum_{bit=1} x_q; the +-1 product follows exactly as
@@ -22,25 +22,42 @@
 //  * K is split across the workgroup's waves (16-byte chunks, 4 lane groups per
 //    wave); the per-wave partial tiles are summed through LDS, then the fused
 //    epilogue applies s_w, the LoRA up-projection and s_x and writes fp32 y.
-//  * Packed weight loads are 16 bytes per lane, 64-byte contiguous runs per row per
-//    instruction, and the next tile's loads are issued before the current tile's
-//    MFMAs.
+//  * Memory pipeline: rows go in stages of T 16-row tiles.  Packed-sign loads are
+//    16 bytes per lane (64-byte runs per row per instruction), issued two stages
+//    ahead of their use from clamped always-valid addresses (never masked, so never
+//    waited for early), and the barriers between stages order LDS only, so the
+//    prefetched loads stay in flight across them.
 #include "device_common.h"
 
 namespace dfssm {
 
+// Rows one workgroup owns at most (their epilogue operands live in LDS).
+constexpr int kGemvRowsPerWG = 1024;
+
 // One lane group = 16 lanes; one chunk = 16 packed bytes = 128 k of one row.
-template <int W, int C, bool kFast>
+// W waves split K; C chunks per lane; T row tiles (16 rows each) per stage.
+template <int W, int C, int T, bool kFast>
 __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     const int8_t* __restrict__ x_q, const float* __restrict__ s_x, int M, int64_t N, int64_t K,
     const uint8_t* __restrict__ w_bits, const float* __restrict__ s_w,
     const int8_t* __restrict__ w_a, const float* __restrict__ s_a, const float* __restrict__ s_b,
     const int32_t* __restrict__ t, int rank, float* __restrict__ y, int32_t* __restrict__ acc_dbg,
-    int64_t num_tiles, int tiles_per_wg) {
-    __shared__ int32_t red[W][16][17];
+    int64_t num_tiles, int stages_per_wg) {
+    // epilogue: thread -> one row of the stage (its W_A row, s_A, s_w are loaded once per
+    // stage) and E of that row's tokens
+    static_assert((W * kWave) % (T * 16) == 0, "a stage's rows must divide the group size");
+    constexpr int E = (T * 16 * 16 + W * kWave - 1) / (W * kWave);
+    constexpr int kTokStride = W * kWave / (T * 16);
+
+    // per-row epilogue operands of every row this group owns, staged once at setup
+    __shared__ uint4 wa_lds[kGemvRowsPerWG];
+    __shared__ float sa_lds[kGemvRowsPerWG];
+    __shared__ float sw_lds[kGemvRowsPerWG];
+    __shared__ int32_t red[W][T * 16][17];
     __shared__ int32_t xs_part[W][kWave];
     __shared__ int32_t xsum[16];
     __shared__ float u[16][kRank];
+    __shared__ float sxs[16];
 
     // problem blockIdx.y of a dense batch (every operand advanced by its own size)
     {
@@ -64,12 +81,96 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     const int i = lane & 15;
     const int g = lane >> 4;
     const int64_t RB = K / 8;
+    const int64_t num_stages = (num_tiles + T - 1) / T;
+    const int64_t st_begin = (int64_t)blockIdx.x * stages_per_wg;
+    const int64_t st_end = st_begin + stages_per_wg < num_stages ? st_begin + stages_per_wg : num_stages;
+    const int erow = threadIdx.x % (T * 16);
+    const int etok0 = threadIdx.x / (T * 16);
 
-    // LoRA: u[tok][r] = s_B[r] * t[tok][r] (fp32), shared by every output row.
-    for (int e = threadIdx.x; e < 16 * kRank; e += W * kWave) {
-        const int tok = e / kRank, r = e % kRank;
-        u[tok][r] = (rank != 0 && tok < M) ? s_b[r] * (float)t[tok * kRank + r] : 0.0f;
+    // packed-sign loads of one stage: T tiles x C chunks, 16 bytes per lane.  The fast
+    // path loads through a buffer resource over this problem's signs: offsets advance
+    // by a constant per stage, rows past N read zero from the range check, and the
+    // values are never masked or used early, so prefetched stages stay in flight.
+    // Chunks past K (lane groups with no chunk) read a valid chunk of the row and meet
+    // all-zero activations.
+    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(w_bits, (uint32_t)(N * RB));
+    int lane_off[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int64_t q = ((int64_t)c * W + wave) * 4 + g;
+        lane_off[c] = (int)((int64_t)i * RB + (16 * q < RB ? 16 * q : 0));
     }
+    const int stage_bytes = (int)(T * 16 * RB);
+    auto load_stage = [&](int64_t st, uint4 (&wv)[T][C]) {
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+            if constexpr (kFast) {
+                const int base = (int)(st * stage_bytes) + (int)(tt * 16 * RB);
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, base + lane_off[c], 0, 0);
+                    wv[tt][c] = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+                }
+            } else {
+                const int64_t n = (st * T + tt) * 16 + i;
+                const uint8_t* row = w_bits + (n < N ? n : N - 1) * RB;
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    const int64_t q = ((int64_t)c * W + wave) * 4 + g;
+                    wv[tt][c] = (n < N) ? load16_guarded<false>(row, 16 * q, RB) : make_uint4(0u, 0u, 0u, 0u);
+                }
+            }
+        }
+    };
+
+    // Stages hold packed signs only; they are prefetched two ahead into three named
+    // buffers that rotate by name, never by copy (a copy of an in-flight register
+    // would wait for its load).  The first two are in flight during the setup.
+    struct Stage {
+        uint4 w[T][C];
+    };
+    auto prefetch = [&](int64_t st, Stage& b) { load_stage(st, b.w); };
+    Stage s0, s1, s2;
+    prefetch(st_begin, s0);  // every group has at least one stage
+    prefetch(st_begin + 1 < st_end ? st_begin + 1 : st_end - 1, s1);
+
+    // the group's rows: W_A row, s_A and s_w into LDS (rank 0: zero LoRA operands)
+    const int64_t row0 = st_begin * T * 16;
+    const int nrows = (int)((st_end - st_begin) * T * 16);
+    for (int r = threadIdx.x; r < nrows; r += W * kWave) {
+        const int64_t n = row0 + r;
+        const bool live = n < N;
+        const int64_t nc = live ? n : N - 1;
+        sw_lds[r] = s_w[nc];
+        if (rank != 0) {
+            wa_lds[r] = *reinterpret_cast<const uint4*>(w_a + nc * kRank);
+            sa_lds[r] = s_a[nc];
+        } else {
+            wa_lds[r] = make_uint4(0u, 0u, 0u, 0u);
+            sa_lds[r] = 0.0f;
+        }
+    }
+
+    // token scales and the LoRA down-projection: loaded now, stored to LDS after the
+    // activation loads below have been issued too
+    constexpr int U = (16 * kRank + W * kWave - 1) / (W * kWave);
+    float tv[U], sbv[U];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+        const int e = threadIdx.x + q * W * kWave;
+        const int tok = e / kRank, r = e % kRank;
+        const bool live = e < 16 * kRank && tok < M;
+        if (rank != 0) {
+            const uint32_t m = opaque_mask(live);
+            tv[q] = (float)(int32_t)((uint32_t)t[(live ? tok : 0) * kRank + r] & m);
+            sbv[q] = __uint_as_float(__float_as_uint(s_b[r]) & m);
+        } else {
+            tv[q] = 0.0f;
+            sbv[q] = 0.0f;
+        }
+    }
+    const float sxv = __uint_as_float(__float_as_uint(s_x[threadIdx.x < M ? threadIdx.x : 0]) &
+                                      opaque_mask(threadIdx.x < M));
 
     // Activations of token i in bit-plane order, for this lane's chunks.
     v4i X[C][8];
@@ -83,7 +184,8 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
         uint32_t nat[32];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const uint4 v = load16_guarded(xrow, kb + 16 * e, xlimit, kFast);
+            const uint4 v = kFast ? load16_select(xrow, kb + 16 * e, kb + 16 * e < xlimit)
+                                  : load16_guarded<false>(xrow, kb + 16 * e, xlimit);
             nat[4 * e + 0] = v.x;
             nat[4 * e + 1] = v.y;
             nat[4 * e + 2] = v.z;
@@ -105,108 +207,145 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
             }
         }
     }
+    // LoRA: u[tok][r] = s_B[r] * t[tok][r] (fp32), shared by every output row.
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+        const int e = threadIdx.x + q * W * kWave;
+        if (e < 16 * kRank) u[e / kRank][e % kRank] = sbv[q] * tv[q];
+    }
+    if (threadIdx.x < 16) sxs[threadIdx.x] = sxv;
     xs_part[wave][lane] = xpart;
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x < 16) {
         int32_t s = 0;
         for (int w = 0; w < W; ++w)
             for (int gg = 0; gg < 4; ++gg) s += xs_part[w][16 * gg + threadIdx.x];
         xsum[threadIdx.x] = s;
     }
-    // (xsum is read after the first tile's barrier below)
+    // (xsum is read after the first stage's barrier below)
 
-    const int64_t tile_begin = (int64_t)blockIdx.x * tiles_per_wg;
-    const int64_t tile_end = tile_begin + tiles_per_wg < num_tiles ? tile_begin + tiles_per_wg : num_tiles;
+    // Outputs through buffer resources: dead elements store to an out-of-range offset.
+    const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(y, (uint32_t)(M * N * 4));
+    const __amdgpu_buffer_rsrc_t acc_rsrc = make_rsrc(acc_dbg, acc_dbg ? (uint32_t)(M * N * 4) : 0u);
 
-    auto load_tile = [&](int64_t tile, uint4 (&wv)[C]) {
-        const int64_t n = tile * 16 + i;
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const int64_t q = ((int64_t)c * W + wave) * 4 + g;
-            wv[c] = (n < N) ? load16_guarded(w_bits + n * RB, 16 * q, RB, kFast) : make_uint4(0u, 0u, 0u, 0u);
-        }
-    };
+    // One stage: issue the prefetch two ahead into `nxt2` (a clamped stage index past
+    // the group's range re-reads its last stage, so the load is unconditional), then
+    // consume `cur`.  Branches below hold no global loads -- only LDS traffic, ALU work
+    // and buffer stores -- so the compiler's waits stay partial across them and the
+    // prefetched stages remain in flight.
+    auto run_stage = [&](int64_t st, Stage& cur, Stage& nxt2) {
+        prefetch(st + 2 < st_end ? st + 2 : st_end - 1, nxt2);
+        if (st >= st_end) return;  // uniform: stage past the group's range
 
-    uint4 wcur[C];
-    if (tile_begin < tile_end) load_tile(tile_begin, wcur);
-    for (int64_t tile = tile_begin; tile < tile_end; ++tile) {
-        uint4 wnext[C];
-        if (tile + 1 < tile_end) load_tile(tile + 1, wnext);
-
-        v4i acc[8];
+        const int32_t one = opaque_one();
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = (v4i){0, 0, 0, 0};
+        for (int tt = 0; tt < T; ++tt) {
+            // planes j and j+4 share accumulator j (weight bytes 2^j * bit):
+            // low planes from w, high planes from w >> 4 under the same masks
+            v4i acc[4];
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
+            for (int j = 0; j < 4; ++j) acc[j] = (v4i){0, 0, 0, 0};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t msk = 0x01010101u << j;
-                const v4i a = {(int)(wcur[c].x & msk), (int)(wcur[c].y & msk),
-                               (int)(wcur[c].z & msk), (int)(wcur[c].w & msk)};
-                acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, X[c][j], acc[j], 0, 0, 0);
-            }
-        }
-        // D[4g + v][i]: scaffold row 4g+v of the tile, token i.
+            for (int c = 0; c < C; ++c) {
+                const uint4 lo = cur.w[tt][c];
+                const uint4 hi = make_uint4(lo.x >> 4, lo.y >> 4, lo.z >> 4, lo.w >> 4);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            int32_t s = -(acc[7][v] >> 7);
+                for (int half = 0; half < 2; ++half) {
+                    const uint4 wv = half ? hi : lo;
 #pragma unroll
-            for (int j = 0; j < 7; ++j) s += acc[j][v] >> j;
-            red[wave][4 * g + v][i] = s;
-        }
-        __syncthreads();
-        for (int e = threadIdx.x; e < 16 * M; e += W * kWave) {
-            const int row = e & 15, tok = e >> 4;
-            const int64_t n = tile * 16 + row;
-            if (n < N) {
-                int32_t s1 = 0;
-#pragma unroll
-                for (int w = 0; w < W; ++w) s1 += red[w][row][tok];
-                const int32_t acc_pm = 2 * s1 - xsum[tok];
-                if (acc_dbg) acc_dbg[(int64_t)tok * N + n] = acc_pm;
-                float lora = 0.0f;
-                if (rank != 0) {
-                    const uint4 wa = *reinterpret_cast<const uint4*>(w_a + n * kRank);
-                    const uint32_t words[4] = {wa.x, wa.y, wa.z, wa.w};
-#pragma unroll
-                    for (int r = 0; r < kRank; ++r) {
-                        const float a = (float)(int8_t)(words[r >> 2] >> (8 * (r & 3)));
-                        lora = fmaf(a, u[tok][r], lora);
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t msk = 0x01010101u << j;
+                        const v4i a = {(int)(wv.x & msk), (int)(wv.y & msk), (int)(wv.z & msk), (int)(wv.w & msk)};
+                        acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, X[c][j + 4 * half], acc[j], 0, 0, 0);
                     }
                 }
-                const float inner = rank != 0 ? fmaf(s_a[n], lora, s_w[n] * (float)acc_pm)
-                                              : s_w[n] * (float)acc_pm;
-                y[(int64_t)tok * N + n] = s_x[tok] * inner;
+            }
+            // D[4g + v][i]: row 4g+v of tile tt, token i; sum_j acc_j / 2^j, exactly
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                // Horner form, three v_lshl_add_u32 per value: 8 acc0 + 4 acc1 + 2 acc2 + acc3
+                const int32_t s8b = (((((acc[0][v] << one) + acc[1][v]) << one) + acc[2][v]) << one) + acc[3][v];
+                red[wave][tt * 16 + 4 * g + v][i] = s8b >> 3;
             }
         }
-        __syncthreads();
+        lds_barrier();
+        const int64_t n = st * T * 16 + erow;
+        const int lrow = (int)(n - row0);
+        const uint4 wa = wa_lds[lrow];
+        const float sa = sa_lds[lrow], sw = sw_lds[lrow];
+        const uint32_t words[4] = {wa.x, wa.y, wa.z, wa.w};
 #pragma unroll
-        for (int c = 0; c < C; ++c) wcur[c] = wnext[c];
+        for (int q = 0; q < E; ++q) {
+            const int tok = etok0 + q * kTokStride;  // uniform per wave when a stage is 64 rows
+            if (tok < M) {
+                int32_t s1 = 0;
+#pragma unroll
+                for (int w = 0; w < W; ++w) s1 += red[w][erow][tok];
+                const int32_t acc_pm = 2 * s1 - xsum[tok];
+                // LoRA up (u and W_A are zero at rank 0, leaving the scaffold term exact)
+                float lora = 0.0f;
+#pragma unroll
+                for (int r = 0; r < kRank; ++r) {
+                    const float a = (float)(int8_t)(words[r >> 2] >> (8 * (r & 3)));
+                    lora = fmaf(a, u[tok][r], lora);
+                }
+                const float inner = fmaf(sa, lora, sw * (float)acc_pm);
+                const int off = n < N ? (int)(((int64_t)tok * N + n) * 4) : kOffDead;
+                store_i32(acc_pm, acc_rsrc, off);
+                store_f32(sxs[tok] * inner, y_rsrc, off);
+            }
+        }
+        lds_barrier();
+    };
+
+    // three stages per trip so the buffers rotate by name
+    for (int64_t st = st_begin; st < st_end; st += 3) {
+        run_stage(st, s0, s2);
+        run_stage(st + 1, s1, s0);
+        run_stage(st + 2, s2, s1);
     }
 }
 
-template <int W, int C>
-static hipError_t launch_gemv_wc(bool fast, const int8_t* x_q, const float* s_x, int M, int64_t N,
-                                 int64_t K, const uint8_t* w_bits, const float* s_w, const int8_t* w_a,
-                                 const float* s_a, const float* s_b, const int32_t* t, int rank,
-                                 float* y, int32_t* acc_dbg, int64_t batch, hipStream_t stream) {
-    // Enough workgroups to fill 256 CUs several times over; beyond that each group
-    // takes more row tiles, which amortizes its activation setup.
+template <int W, int C, int T>
+static hipError_t launch_gemv_wct(bool fast, const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
+                                  const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
+                                  const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
+                                  int64_t batch, hipStream_t stream) {
     const int64_t num_tiles = (N + 15) / 16;
+    const int64_t num_stages = (num_tiles + T - 1) / T;
+    // ~8 groups per CU in flight overall; beyond that, groups take more stages,
+    // which amortizes their activation setup
     const int64_t target_wgs = 2048;
     const int64_t per_problem = (target_wgs + batch - 1) / batch;
-    const int tiles_per_wg = (int)((num_tiles + per_problem - 1) / per_problem);
-    const dim3 grid((unsigned)((num_tiles + tiles_per_wg - 1) / tiles_per_wg), (unsigned)batch);
+    int stages_per_wg = (int)((num_stages + per_problem - 1) / per_problem);
+    if (stages_per_wg * T * 16 > kGemvRowsPerWG) stages_per_wg = kGemvRowsPerWG / (T * 16);
+    const dim3 grid((unsigned)((num_stages + stages_per_wg - 1) / stages_per_wg), (unsigned)batch);
     if (fast) {
-        gemv_kernel<W, C, true><<<grid, W * kWave, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b,
-                                                                t, rank, y, acc_dbg, num_tiles, tiles_per_wg);
+        gemv_kernel<W, C, T, true><<<grid, W * kWave, 0, stream>>>(
+            x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, num_tiles, stages_per_wg);
     } else {
-        gemv_kernel<W, C, false><<<grid, W * kWave, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b,
-                                                                 t, rank, y, acc_dbg, num_tiles, tiles_per_wg);
+        gemv_kernel<W, C, T, false><<<grid, W * kWave, 0, stream>>>(
+            x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, num_tiles, stages_per_wg);
     }
     return hipGetLastError();
 }
 
+template <int W, int C>
+static hipError_t launch_gemv_wc(bool fast, const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
+                                 const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
+                                 const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
+                                 int64_t batch, hipStream_t stream) {
+    // Few tiles overall (one decode call): one tile per stage spreads the rows over
+    // the most CUs.  Many tiles (batched calls): four tiles per stage keep more
+    // packed-sign loads in flight per wave.
+    constexpr int kTBig = (W >= 4 && C <= 2) ? 4 : 1;
+    const int64_t total_tiles = batch * ((N + 15) / 16);
+    if (total_tiles <= 4096)
+        return launch_gemv_wct<W, C, 1>(fast, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg,
+                                        batch, stream);
+    return launch_gemv_wct<W, C, kTBig>(fast, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg,
+                                        batch, stream);
+}
 
 hipError_t launch_gemv(const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
                        const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,

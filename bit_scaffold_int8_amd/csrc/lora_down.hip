@@ -40,8 +40,8 @@ __global__ __launch_bounds__(kLoraWaves * kWave) void lora_down_kernel(
     const int64_t steps = (K + 63) / 64;
     for (int64_t s = wave; s < steps; s += kLoraWaves) {
         const int64_t off = s * 64 + 16 * g;
-        const uint4 a = load16_guarded(xrow, off, xlimit, kFast);
-        const uint4 b = load16_guarded(brow, off, K, kFast);
+        const uint4 a = load16_guarded<kFast>(xrow, off, xlimit);
+        const uint4 b = load16_guarded<kFast>(brow, off, K);
         const v4i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
         const v4i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w};
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);

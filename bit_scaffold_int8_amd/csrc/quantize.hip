@@ -18,18 +18,53 @@ namespace dfssm {
 constexpr int kQuantThreads = 256;
 constexpr int kVecPerThread = 4;  // K <= 4096 stays in registers
 
-__device__ __forceinline__ int8_t quantize_one(float v, float s) {
-    float r = rintf(v / s);  // IEEE division (correctly rounded), round half to even
+// Code of one element: rint(fl(v / s)) clamped to [-127, 127] (round half to even).
+__device__ __forceinline__ int8_t exact_code(float v, float s) {
+    float r = rintf(v / s);  // IEEE division (correctly rounded), ties to even
     r = fminf(fmaxf(r, -127.0f), 127.0f);
     return (int8_t)(int)r;
 }
 
-__device__ __forceinline__ uint32_t quantize4(float4 v, float s) {
-    uint32_t b0 = (uint8_t)quantize_one(v.x, s);
-    uint32_t b1 = (uint8_t)quantize_one(v.y, s);
-    uint32_t b2 = (uint8_t)quantize_one(v.z, s);
-    uint32_t b3 = (uint8_t)quantize_one(v.w, s);
+// The same code from a multiply: with inv = fl(1 / s) and |v / s| <= 127 (+ rounding),
+// |fl(v * inv) - fl(v / s)| is at most 0.5 ulp(v/s) + 127 * 2^-24 + 0.5 ulp(v*inv)
+// < 1.6e-5.  The two can only round to different integers if a half-integer lies
+// between them, i.e. within 1.6e-5 of fl(v * inv).  Such elements are flagged in
+// `near` (margin 2^-15 = 3.05e-5) and must be redone with exact_code; all others
+// are bit-identical to the IEEE quotient's code.
+__device__ __forceinline__ uint32_t fast_code(float v, float inv, bool& near) {
+    const float r = v * inv;
+    const float f = r - floorf(r);  // exact: the fraction bits of r
+    near = fabsf(f - 0.5f) <= 0x1p-15f;
+    const float q = fminf(fmaxf(rintf(r), -127.0f), 127.0f);
+    return (uint32_t)(uint8_t)(int8_t)(int)q;
+}
+
+// Four codes packed little-endian; bit c of `near4` flags element c.
+__device__ __forceinline__ uint32_t fast_code4(float4 v, float inv, uint32_t& near4) {
+    bool n0, n1, n2, n3;
+    const uint32_t b0 = fast_code(v.x, inv, n0), b1 = fast_code(v.y, inv, n1);
+    const uint32_t b2 = fast_code(v.z, inv, n2), b3 = fast_code(v.w, inv, n3);
+    near4 = (uint32_t)n0 | ((uint32_t)n1 << 1) | ((uint32_t)n2 << 2) | ((uint32_t)n3 << 3);
     return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+__device__ __forceinline__ uint32_t exact_code4(float4 v, float s) {
+    return (uint32_t)(uint8_t)exact_code(v.x, s) | ((uint32_t)(uint8_t)exact_code(v.y, s) << 8) |
+           ((uint32_t)(uint8_t)exact_code(v.z, s) << 16) | ((uint32_t)(uint8_t)exact_code(v.w, s) << 24);
+}
+
+// Row scale, its reciprocal, and whether the multiply path is usable for the row.
+struct RowScale {
+    float s, inv;
+    bool fast;
+};
+
+__device__ __forceinline__ RowScale row_scale(float amax) {
+    RowScale r;
+    r.s = amax / 127.0f;  // one IEEE division
+    r.inv = 1.0f / r.s;
+    r.fast = isfinite(r.inv);
+    return r;
 }
 
 // Block-wide max over kQuantThreads lanes; every lane gets the result.
@@ -81,16 +116,33 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_act_kernel(
             if (tid == 0) s_x[m] = 0.0f;
             return;
         }
-        const float s = amax / 127.0f;
-        if (tid == 0) s_x[m] = s;
+        const RowScale rs = row_scale(amax);
+        if (tid == 0) s_x[m] = rs.s;
         if (in_regs) {
+            uint32_t near = 0;  // bit 4i+c: element c of float4 i needs the exact quotient
 #pragma unroll
             for (int i = 0; i < kVecPerThread; ++i) {
                 const int64_t idx = tid + (int64_t)i * kQuantThreads;
-                if (idx < K4) q4[idx] = quantize4(v[i], s);
+                if (idx < K4) {
+                    uint32_t n4;
+                    q4[idx] = fast_code4(v[i], rs.inv, n4);
+                    near |= (rs.fast ? n4 : 0xFu) << (4 * i);
+                }
+            }
+            while (near) {  // rare: redo flagged elements exactly (same thread, same bytes)
+                const int bit = __builtin_ctz(near);
+                near &= near - 1;
+                const int64_t k = 4 * (tid + (int64_t)(bit >> 2) * kQuantThreads) + (bit & 3);
+                qrow[k] = exact_code(row[k], rs.s);
             }
         } else {
-            for (int64_t idx = tid; idx < K4; idx += kQuantThreads) q4[idx] = quantize4(row4[idx], s);
+            for (int64_t idx = tid; idx < K4; idx += kQuantThreads) {
+                const float4 xv = row4[idx];
+                uint32_t n4;
+                uint32_t q = fast_code4(xv, rs.inv, n4);
+                if (!rs.fast || n4) q = exact_code4(xv, rs.s);
+                q4[idx] = q;
+            }
         }
     } else {
         float amax = 0.0f;
@@ -103,7 +155,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_act_kernel(
         }
         const float s = amax / 127.0f;
         if (tid == 0) s_x[m] = s;
-        for (int64_t k = tid; k < K; k += kQuantThreads) qrow[k] = quantize_one(row[k], s);
+        for (int64_t k = tid; k < K; k += kQuantThreads) qrow[k] = exact_code(row[k], s);
     }
 }
 
@@ -135,7 +187,8 @@ namespace dfssm {
 constexpr int kQLWaves = 8;
 constexpr int kQLThreads = kQLWaves * kWave;
 constexpr int64_t kQLLdsBytes = 65536 - 1024;  // codes; the rest of 64 KiB holds the t tile
-constexpr int kQLRegVec = 16;  // float4 per lane kept in registers (K <= 4096)
+constexpr int kQLRegVec = 16;  // float4 per lane kept in registers (K <= 4096 at a wave per row)
+constexpr int kQLPre = 8;      // W_B fragments per wave fetched ahead (covers K <= 4096)
 
 __device__ __forceinline__ float absmax4(float4 v) {
     return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
@@ -146,6 +199,7 @@ __global__ __launch_bounds__(kQLThreads) void quantize_lora_down_kernel(
     int8_t* __restrict__ x_q, float* __restrict__ s_x, int32_t* __restrict__ t, int tokens_per_group) {
     extern __shared__ __align__(16) uint8_t lds_q[];  // [tokens_per_group][K] codes
     __shared__ int32_t tsum[16][16];                   // t tile [token][rank], summed over waves
+    __shared__ float amax_part[kQLWaves];
 
     const int64_t p = blockIdx.y;  // problem of a dense batch
     x += p * M * K;
@@ -163,43 +217,94 @@ __global__ __launch_bounds__(kQLThreads) void quantize_lora_down_kernel(
     const int64_t K4 = K / 4;
     if (threadIdx.x < 256) tsum[threadIdx.x >> 4][threadIdx.x & 15] = 0;
 
-    // ---- phase 1: each wave quantizes rows wave, wave + 8, ...
-    for (int r = wave; r < rows; r += kQLWaves) {
-        const int64_t m = m0 + r;
+    // W_B does not depend on x: its first fragments are fetched before the row loads
+    const int i = lane & 15, g = lane >> 4;
+    const uint8_t* brow = reinterpret_cast<const uint8_t*>(w_b) + (int64_t)i * K;
+    const int64_t steps = (K + 63) / 64;
+    const bool rows16 = (K % 16) == 0;  // 16-byte aligned rows in LDS and in W_B
+    auto load_b = [&](int64_t st) -> uint4 {
+        const int64_t off = st * 64 + 16 * g;
+        if (rank == 0 || st >= steps || off >= K) return make_uint4(0u, 0u, 0u, 0u);
+        if (rows16 && off + 16 <= K) return *reinterpret_cast<const uint4*>(brow + off);
+        uint32_t bw[4] = {0u, 0u, 0u, 0u};
+        for (int e = 0; e < 4; ++e)
+            if (off + 4 * e < K) bw[e] = *reinterpret_cast<const uint32_t*>(brow + off + 4 * e);
+        return make_uint4(bw[0], bw[1], bw[2], bw[3]);
+    };
+    uint4 bpre[kQLPre];
+#pragma unroll
+    for (int u = 0; u < kQLPre; ++u) bpre[u] = load_b(wave + (int64_t)u * kQLWaves);
+
+    // ---- phase 1: quantize the group's rows.  Few rows (decode): several waves
+    // share a row and combine their absmax through LDS; many rows: a wave per row.
+    const int wpr = rows >= 8 ? 1 : (rows >= 4 ? 2 : (rows >= 2 ? 4 : 8));  // waves per row
+    const int rpp = kQLWaves / wpr;                                           // rows per pass
+    const int sub = wave % wpr;
+    const int64_t lstride = (int64_t)wpr * kWave;  // float4 stride of one lane within its row
+    const bool in_regs = K4 <= lstride * kQLRegVec;
+    for (int r0 = 0; r0 < rows; r0 += rpp) {
+        const int r = r0 + wave / wpr;
+        const bool live = r < rows;
+        const int64_t m = m0 + (live ? r : 0);
         const float4* row4 = reinterpret_cast<const float4*>(x + m * K);
         uint32_t* q4 = reinterpret_cast<uint32_t*>(x_q + m * K);
-        uint32_t* l4 = reinterpret_cast<uint32_t*>(lds_q + (int64_t)r * K);
-        const bool in_regs = K4 <= (int64_t)kWave * kQLRegVec;
+        uint32_t* l4 = reinterpret_cast<uint32_t*>(lds_q + (int64_t)(live ? r : 0) * K);
+        const int64_t lbase = (int64_t)sub * kWave + lane;
         float4 v[kQLRegVec];
         float amax = 0.0f;
-        if (in_regs) {
+        if (live) {
+            if (in_regs) {
 #pragma unroll
-            for (int i = 0; i < kQLRegVec; ++i) {
-                const int64_t idx = lane + (int64_t)i * kWave;
-                v[i] = idx < K4 ? row4[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
-                amax = fmaxf(amax, absmax4(v[i]));
+                for (int e = 0; e < kQLRegVec; ++e) {
+                    const int64_t idx = lbase + (int64_t)e * lstride;
+                    v[e] = idx < K4 ? row4[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    amax = fmaxf(amax, absmax4(v[e]));
+                }
+            } else {
+                for (int64_t idx = lbase; idx < K4; idx += lstride) amax = fmaxf(amax, absmax4(row4[idx]));
             }
-        } else {
-            for (int64_t idx = lane; idx < K4; idx += kWave) amax = fmaxf(amax, absmax4(row4[idx]));
         }
         amax = wave_max(amax);
-        const float s = amax / 127.0f;
-        if (lane == 0) s_x[m] = amax == 0.0f ? 0.0f : s;
-        if (in_regs) {
+        if (lane == 0) amax_part[wave] = amax;
+        __syncthreads();
+        const int w0 = (wave / wpr) * wpr;
+        for (int w = 0; w < wpr; ++w) amax = fmaxf(amax, amax_part[w0 + w]);
+        __syncthreads();  // amax_part is rewritten by the next pass
+        if (live) {
+            const RowScale rs = row_scale(amax);
+            if (lane == 0 && sub == 0) s_x[m] = amax == 0.0f ? 0.0f : rs.s;
+            if (in_regs) {
+                uint64_t near = 0;  // bit 4e+c: element c of float4 e needs the exact quotient
 #pragma unroll
-            for (int i = 0; i < kQLRegVec; ++i) {
-                const int64_t idx = lane + (int64_t)i * kWave;
-                if (idx < K4) {
-                    const uint32_t q = amax == 0.0f ? 0u : quantize4(v[i], s);
+                for (int e = 0; e < kQLRegVec; ++e) {
+                    const int64_t idx = lbase + (int64_t)e * lstride;
+                    if (idx < K4) {
+                        uint32_t n4 = 0;
+                        const uint32_t q = amax == 0.0f ? 0u : fast_code4(v[e], rs.inv, n4);
+                        q4[idx] = q;
+                        l4[idx] = q;
+                        if (amax != 0.0f) near |= (uint64_t)(rs.fast ? n4 : 0xFu) << (4 * e);
+                    }
+                }
+                int8_t* qb = x_q + m * K;
+                int8_t* lb = reinterpret_cast<int8_t*>(lds_q) + (int64_t)r * K;
+                while (near) {  // rare: redo flagged elements exactly (same thread, same bytes)
+                    const int bit = __builtin_ctzll(near);
+                    near &= near - 1;
+                    const int64_t k = 4 * (lbase + (int64_t)(bit >> 2) * lstride) + (bit & 3);
+                    const int8_t c = exact_code(x[m * K + k], rs.s);
+                    qb[k] = c;
+                    lb[k] = c;
+                }
+            } else {
+                for (int64_t idx = lbase; idx < K4; idx += lstride) {
+                    const float4 xv = row4[idx];
+                    uint32_t n4 = 0;
+                    uint32_t q = amax == 0.0f ? 0u : fast_code4(xv, rs.inv, n4);
+                    if (amax != 0.0f && (!rs.fast || n4)) q = exact_code4(xv, rs.s);
                     q4[idx] = q;
                     l4[idx] = q;
                 }
-            }
-        } else {
-            for (int64_t idx = lane; idx < K4; idx += kWave) {
-                const uint32_t q = amax == 0.0f ? 0u : quantize4(row4[idx], s);
-                q4[idx] = q;
-                l4[idx] = q;
             }
         }
     }
@@ -207,34 +312,27 @@ __global__ __launch_bounds__(kQLThreads) void quantize_lora_down_kernel(
     __syncthreads();
 
     // ---- phase 2: t tile = codes (16 tokens, LDS) x W_B^T (16 ranks, global)
-    const int i = lane & 15, g = lane >> 4;
     const uint8_t* arow = lds_q + (int64_t)i * K;
     const bool arow_live = i < rows;
-    const uint8_t* brow = reinterpret_cast<const uint8_t*>(w_b) + (int64_t)i * K;
-    v4i acc = {0, 0, 0, 0};
-    const int64_t steps = (K + 63) / 64;
-    const bool rows16 = (K % 16) == 0;  // 16-byte aligned rows in LDS and in W_B
-    for (int64_t st = wave; st < steps; st += kQLWaves) {
+    auto load_a = [&](int64_t st) -> uint4 {
         const int64_t off = st * 64 + 16 * g;
-        uint4 a = make_uint4(0u, 0u, 0u, 0u), b = make_uint4(0u, 0u, 0u, 0u);
-        if (rows16 && off + 16 <= K) {
-            if (arow_live) a = *reinterpret_cast<const uint4*>(arow + off);
-            b = *reinterpret_cast<const uint4*>(brow + off);
-        } else if (off < K) {  // rows only 4-byte aligned, or the K tail: word by word
-            uint32_t aw[4] = {0u, 0u, 0u, 0u}, bw[4] = {0u, 0u, 0u, 0u};
-            for (int e = 0; e < 4; ++e) {
-                if (off + 4 * e < K) {
-                    if (arow_live) aw[e] = *reinterpret_cast<const uint32_t*>(arow + off + 4 * e);
-                    bw[e] = *reinterpret_cast<const uint32_t*>(brow + off + 4 * e);
-                }
-            }
-            a = make_uint4(aw[0], aw[1], aw[2], aw[3]);
-            b = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-        }
+        if (!arow_live || st >= steps || off >= K) return make_uint4(0u, 0u, 0u, 0u);
+        if (rows16 && off + 16 <= K) return *reinterpret_cast<const uint4*>(arow + off);
+        uint32_t aw[4] = {0u, 0u, 0u, 0u};
+        for (int e = 0; e < 4; ++e)
+            if (off + 4 * e < K) aw[e] = *reinterpret_cast<const uint32_t*>(arow + off + 4 * e);
+        return make_uint4(aw[0], aw[1], aw[2], aw[3]);
+    };
+    auto mfma = [](uint4 a, uint4 b, v4i acc) {
         const v4i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
         const v4i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w};
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
-    }
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc, 0, 0, 0);
+    };
+    v4i acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < kQLPre; ++u) acc = mfma(load_a(wave + (int64_t)u * kQLWaves), bpre[u], acc);
+    for (int64_t st = wave + (int64_t)kQLPre * kQLWaves; st < steps; st += kQLWaves)
+        acc = mfma(load_a(st), load_b(st), acc);
     // D[4g + v][i] = t[token 4g+v][rank i]; integer adds commute, so LDS atomics
     // give the exact sum in any order
 #pragma unroll

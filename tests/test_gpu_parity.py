@@ -250,3 +250,53 @@ def test_repeated_calls_are_deterministic(torch_cuda):
     a, b = _run_hip(prob), _run_hip(prob)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def _near_tie_rows(K=1024):
+    """Rows whose quotients x/s land within a few ulps of half-integers, for several
+    scales (including one whose reciprocal overflows fp32)."""
+    rng = np.random.default_rng(4242)
+    rows = []
+    for amax in (100.0, 3.7, 1e-3, 5.0e4, 1e-39):
+        s = np.float32(amax) / np.float32(127)
+        vals = [np.float32(amax)]
+        for k in range(-127, 127):
+            c = np.float32((k + 0.5) * np.float64(s))
+            for d in (-2, -1, 0, 1, 2):
+                v = c
+                for _ in range(abs(d)):
+                    v = np.nextafter(v, np.float32(np.inf if d > 0 else -np.inf), dtype=np.float32)
+                vals.append(v)
+        vals = np.array(vals, np.float32)
+        vals = vals[np.abs(vals) <= np.float32(amax)]
+        row = (rng.uniform(-1, 1, K) * amax * 0.5).astype(np.float32)
+        row[:len(vals)] = vals[:K]
+        row[0] = np.float32(amax)
+        rows.append(row)
+    return np.stack(rows)
+
+
+def test_quantizer_near_ties_bit_exact(torch_cuda):
+    import torch
+    from bit_scaffold_int8_amd import dfssm
+    x = _near_tie_rows()
+    M, K = x.shape
+    q_ref, s_ref = oracle.quantize_act(x)
+    xd = torch.from_numpy(x).cuda()
+    x_q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    s_x = torch.empty((M,), dtype=torch.float32, device="cuda")
+    dfssm.dfssm_quantize_act(xd, x_q, s_x)
+    torch.cuda.synchronize()
+    assert np.array_equal(s_x.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(x_q.cpu().numpy(), q_ref)
+    # the fused quantize + LoRA-down kernel, token counts that exercise every
+    # waves-per-row split (1, 2, 4, 8 rows per group and two passes)
+    for m in (1, 2, 3, 5, 9, 16):
+        xs = np.concatenate([x] * 4)[:m]
+        prob = si.make_problem(m, 16, K, 0, seed=m)
+        prob.x = np.ascontiguousarray(xs)
+        got = _run_hip(prob)
+        q2, s2 = oracle.quantize_act(xs)
+        assert np.array_equal(got["s_x"].view(np.uint32), s2.view(np.uint32)), m
+        assert np.array_equal(got["x_q"], q2), m
+        assert np.array_equal(got["t"], oracle.lora_down(q2, prob.W_B)), m
