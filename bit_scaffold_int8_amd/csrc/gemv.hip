@@ -53,7 +53,10 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     __shared__ uint4 wa_lds[kGemvRowsPerWG];
     __shared__ float sa_lds[kGemvRowsPerWG];
     __shared__ float sw_lds[kGemvRowsPerWG];
-    __shared__ int32_t red[W][T * 16][17];
+    // the stage's scaffold sums, added into by every wave (exact integer adds commute).
+    // Row stride 20 words keeps the adds of one instruction (rows 4g+v, tokens i) on
+    // distinct banks.
+    __shared__ int32_t red[1][T * 16][20];
     __shared__ int32_t xs_part[W][kWave];
     __shared__ int32_t xsum[16];
     __shared__ float u[16][kRank];
@@ -215,6 +218,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     }
     if (threadIdx.x < 16) sxs[threadIdx.x] = sxv;
     xs_part[wave][lane] = xpart;
+    for (int e = threadIdx.x; e < T * 16 * 20; e += W * kWave) (&red[0][0][0])[e] = 0;
     lds_barrier();
     if (threadIdx.x < 16) {
         int32_t s = 0;
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     // consume `cur`.  Branches below hold no global loads -- only LDS traffic, ALU work
     // and buffer stores -- so the compiler's waits stay partial across them and the
     // prefetched stages remain in flight.
-    auto run_stage = [&](int64_t st, Stage& cur, Stage& nxt2) {
+    auto run_stage = [&](int64_t st, Stage& cur, Stage& nxt2, int rb) {
         prefetch(st + 2 < st_end ? st + 2 : st_end - 1, nxt2);
         if (st >= st_end) return;  // uniform: stage past the group's range
 
@@ -260,12 +264,15 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
                     }
                 }
             }
-            // D[4g + v][i]: row 4g+v of tile tt, token i; sum_j acc_j / 2^j, exactly
+            // D[4g + v][i]: row 4g+v of tile tt, token i; sum_j acc_j / 2^j, exactly.
+            // Only token lanes (i < M) add; the branch holds no global load.
+            if (i < M) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                // Horner form, three v_lshl_add_u32 per value: 8 acc0 + 4 acc1 + 2 acc2 + acc3
-                const int32_t s8b = (((((acc[0][v] << one) + acc[1][v]) << one) + acc[2][v]) << one) + acc[3][v];
-                red[wave][tt * 16 + 4 * g + v][i] = s8b >> 3;
+                for (int v = 0; v < 4; ++v) {
+                    // Horner form, three v_lshl_add_u32 per value: 8 acc0 + 4 acc1 + 2 acc2 + acc3
+                    const int32_t s8b = (((((acc[0][v] << one) + acc[1][v]) << one) + acc[2][v]) << one) + acc[3][v];
+                    atomicAdd(&red[rb][tt * 16 + 4 * g + v][i], s8b >> 3);
+                }
             }
         }
         lds_barrier();
@@ -278,9 +285,8 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
         for (int q = 0; q < E; ++q) {
             const int tok = etok0 + q * kTokStride;  // uniform per wave when a stage is 64 rows
             if (tok < M) {
-                int32_t s1 = 0;
-#pragma unroll
-                for (int w = 0; w < W; ++w) s1 += red[w][erow][tok];
+                const int32_t s1 = red[rb][erow][tok];
+                red[rb][erow][tok] = 0;  // ready for the stage after next
                 const int32_t acc_pm = 2 * s1 - xsum[tok];
                 // LoRA up (u and W_A are zero at rank 0, leaving the scaffold term exact)
                 float lora = 0.0f;
@@ -295,14 +301,14 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
                 store_f32(sxs[tok] * inner, y_rsrc, off);
             }
         }
-        lds_barrier();
+        lds_barrier();  // the sums are re-added into by the next stage
     };
 
-    // three stages per trip so the buffers rotate by name
+    // three stages per trip so the register buffers rotate by name
     for (int64_t st = st_begin; st < st_end; st += 3) {
-        run_stage(st, s0, s2);
-        run_stage(st + 1, s1, s0);
-        run_stage(st + 2, s2, s1);
+        run_stage(st, s0, s2, 0);
+        run_stage(st + 1, s1, s0, 0);
+        run_stage(st + 2, s2, s1, 0);
     }
 }
 
