@@ -5,6 +5,7 @@
 #include "dfssm.h"
 
 #include <hip/hip_runtime.h>
+#include <stdlib.h>
 
 namespace dfssm {
 hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int8_t* x_q, float* s_x,
@@ -22,6 +23,12 @@ hipError_t launch_gemm_mfma(const int8_t* x_q, const float* s_x, int64_t M, int6
                             const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
                             const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
                             int64_t batch, hipStream_t stream);
+bool prefill_supported(int64_t M, int64_t N, int64_t K);
+int prefill_num_cfgs();
+hipError_t launch_gemm_prefill(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
+                               const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
+                               const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
+                               int64_t batch, int force_cfg, hipStream_t stream);
 }  // namespace dfssm
 
 namespace {
@@ -105,8 +112,20 @@ dfssm_status gemm_impl(const int8_t* x_q, const float* s_x, int64_t M, int64_t N
         e = dfssm::launch_gemv(x_q, s_x, (int)M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch,
                                stream);
     } else {
-        e = dfssm::launch_gemm_mfma(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch,
-                                    stream);
+        // DFSSM_PREFILL_CFG pins the many-token kernel's tile configuration (0 ..
+        // prefill_num_cfgs() - 1) or, with -2, the generic fallback kernel; unset or -1
+        // lets the cost model choose.  A testing and tuning knob.
+        int force = -1;
+        if (const char* f = getenv("DFSSM_PREFILL_CFG")) force = atoi(f);
+        const bool prefill = force != -2 && dfssm::prefill_supported(M, N, K) && aligned16(w_bits) &&
+                             (rank == 0 || aligned16(w_a));
+        if (prefill) {
+            e = dfssm::launch_gemm_prefill(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg,
+                                           batch, force, stream);
+        } else {
+            e = dfssm::launch_gemm_mfma(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch,
+                                        stream);
+        }
     }
     return e == hipSuccess ? DFSSM_OK : DFSSM_ERR_HIP;
 }

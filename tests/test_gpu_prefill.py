@@ -1,0 +1,74 @@
+"""GPU parity of the many-token kernels, each tile configuration pinned in turn.
+
+The dispatcher picks the prefill kernel's tile configuration by a cost model, so
+ordinary calls exercise only some of them; DFSSM_PREFILL_CFG pins one (0 .. n-1,
+or -2 for the generic fallback kernel).  Every configuration must match the CPU
+oracle on the same bar as the rest: x_q, s_x, t and the accumulators bit-exact, y
+within 1e-5 of the magnitude of its terms.
+"""
+import numpy as np
+import pytest
+
+import synth_inputs as si
+from test_gpu_parity import _check_full, torch_cuda  # noqa: F401  (fixture)
+
+pytestmark = pytest.mark.gpu
+
+N_CFGS = 3                      # tile configurations of the prefill kernel
+CFGS = list(range(N_CFGS)) + [-2]
+
+SHAPES = [
+    (17, 1, 64),        # one column, one 64-k slice (half a chunk)
+    (33, 70, 192),      # odd chunk count and a half chunk
+    (100, 513, 1024),   # ragged rows and columns
+    (128, 512, 2048),   # whole tiles
+    (129, 130, 4096),   # one row into the next tile, 32 chunks
+    (300, 1000, 2112),  # several row tiles, ragged K
+]
+
+
+@pytest.mark.parametrize("cfg", CFGS)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_prefill_config_parity(torch_cuda, monkeypatch, cfg, M, N, K):
+    monkeypatch.setenv("DFSSM_PREFILL_CFG", str(cfg))
+    _check_full(si.make_problem(M, N, K, max(1, K // 100), seed=M * 31 + N * 7 + K + 5 * cfg))
+
+
+@pytest.mark.parametrize("cfg", CFGS)
+def test_prefill_config_rank_zero(torch_cuda, monkeypatch, cfg):
+    monkeypatch.setenv("DFSSM_PREFILL_CFG", str(cfg))
+    _check_full(si.make_problem(70, 200, 1024, 10, seed=11 + cfg), rank=0)
+
+
+@pytest.mark.parametrize("cfg", CFGS)
+def test_prefill_config_extreme_accumulators(torch_cuda, monkeypatch, cfg):
+    # every code at +-127 and every sign +1 (or all -1): |acc| = 127 K, the largest
+    # the contraction can produce
+    monkeypatch.setenv("DFSSM_PREFILL_CFG", str(cfg))
+    prob = si.make_problem(40, 96, 2048, 0, seed=3)
+    prob.x = np.where(np.arange(2048)[None, :] % 2 == 0, 1.0, -1.0).astype(np.float32) * np.ones((40, 1), np.float32)
+    prob.x[1::2] = 1.0
+    prob.P[:48] = 0xFF
+    prob.P[48:] = 0x00
+    got, _ = _check_full(prob)
+    assert got["acc"][1, 0] == 127 * 2048 and got["acc"][1, 50] == -127 * 2048
+
+
+@pytest.mark.parametrize("cfg", CFGS)
+def test_prefill_config_batched(torch_cuda, monkeypatch, cfg):
+    import torch
+    from bit_scaffold_int8_amd.runner import DeviceProjections
+    import oracle
+    from test_gpu_parity import _magnitude, _assert_y
+    monkeypatch.setenv("DFSSM_PREFILL_CFG", str(cfg))
+    probs = si.make_copies(65, 300, 512, 5, seed=90 + cfg, copies=3)
+    dp = DeviceProjections.from_problems(probs, with_acc=True)
+    dp.forward()
+    torch.cuda.synchronize()
+    for b, prob in enumerate(probs):
+        xq_ref, sx_ref = oracle.quantize_act(prob.x)
+        y_ref, acc_ref, t_ref = oracle.scaffold_lora_gemm(xq_ref, sx_ref, prob.P, prob.s_w, prob.W_A, prob.s_A,
+                                                          prob.W_B, prob.s_B, nthreads=8)
+        assert np.array_equal(dp.acc_dbg[b].cpu().numpy(), acc_ref), b
+        D = _magnitude(sx_ref, prob.s_w, acc_ref, prob.s_A, prob.W_A, prob.s_B, t_ref)
+        _assert_y(dp.y[b].cpu().numpy(), y_ref, D, f"batch {b}")
