@@ -28,7 +28,7 @@ int prefill_num_cfgs();
 hipError_t launch_gemm_prefill(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                                const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
                                const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                               int64_t batch, int force_cfg, hipStream_t stream);
+                               int64_t batch, int force_cfg, int force_tail, hipStream_t stream);
 }  // namespace dfssm
 
 namespace {
@@ -114,14 +114,16 @@ dfssm_status gemm_impl(const int8_t* x_q, const float* s_x, int64_t M, int64_t N
     } else {
         // DFSSM_PREFILL_CFG pins the many-token kernel's tile configuration (0 ..
         // prefill_num_cfgs() - 1) or, with -2, the generic fallback kernel; unset or -1
-        // lets the cost model choose.  A testing and tuning knob.
-        int force = -1;
+        // lets the cost model choose.  DFSSM_PREFILL_TAIL adds a narrower configuration
+        // for the columns past the pinned one's last whole tile.  Testing and tuning knobs.
+        int force = -1, force_tail = -1;
         if (const char* f = getenv("DFSSM_PREFILL_CFG")) force = atoi(f);
+        if (const char* f = getenv("DFSSM_PREFILL_TAIL")) force_tail = atoi(f);
         const bool prefill = force != -2 && dfssm::prefill_supported(M, N, K) && aligned16(w_bits) &&
                              (rank == 0 || aligned16(w_a));
         if (prefill) {
             e = dfssm::launch_gemm_prefill(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg,
-                                           batch, force, stream);
+                                           batch, force, force_tail, stream);
         } else {
             e = dfssm::launch_gemm_mfma(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch,
                                         stream);

@@ -7,23 +7,31 @@
 // contraction, so it runs on v_mfma_i32_32x32x32_i8; nothing is materialized in memory.
 //
 // Work split.  A workgroup is 4 waves (one per SIMD) and owns a (32 MB) x (32 NB WNW)
-// output tile; WNW = 4 / KS waves side by side along N, KS waves along K (split-K
-// inside the workgroup, reduced through LDS at the end).  Each wave keeps its
+// output tile: WNW = 4 / KS waves side by side along N and KS groups along K
+// (split-K inside the workgroup, summed through LDS at the end).  Each wave keeps its
 // (32 MB) x (32 NB) partial tile in MB x NB accumulators of 16 registers (AGPRs).
 //
-// Operands, straight from memory into registers (no LDS in the main loop):
-//  * A (x_q rows): in a 128-k chunk, lane group g = lane / 32 takes k in
-//    [64 g, 64 g + 64) and MFMA step s its 16 bytes [64 g + 16 s, +16) -- one 16-byte
-//    load per row per step.  Any per-lane k order is valid as long as A and B agree.
-//  * B (signs): the same lane's 64 sign bits of a column are 8 contiguous bytes (one
-//    8-byte load per column per chunk).  Step s takes 16 of them and expands them to
-//    16 bytes of +-1: each nibble is spread to one bit per byte ((nib * 0x00204081)
-//    & 0x01010101) and a byte permute maps 0/1 to 0xFF/0x01.  With +-1 weights the
-//    accumulator is the scaffold sum itself, no row-sum correction.
-//  * 4-deep step rotation: the A registers of step s are reloaded with the next
-//    chunk's step s right after their MFMAs, so loads run one chunk ahead.
-//  * Tails: every load goes through a buffer resource; rows past M, columns past N
-//    and k past K use an offset beyond the resource, which reads zero.
+// Weights as 0/1.  A sign w = 2 b - 1 with bit b, so sum_k w x = 2 S - R with
+// S = sum_k b x (the MFMA product with 0/1 bytes) and R = sum_k x (the token's code
+// sum).  0/1 operand bytes switch far fewer bits than 0x01/0xFF, which lets the
+// matrix cores run measurably faster under the same power limit, and the expansion
+// is one VALU op shorter per word: nibble * 0x00204081 & 0x01010101 spreads four
+// sign bits to four bytes.  R is summed by the threads that stage the codes.
+//
+// Data flow per K group, in 128-k chunks:
+//  * A (codes): staged through LDS, 8 threads per 128-byte row segment (whole cache
+//    lines), rows padded to 144 bytes so the 16 rows one 16-lane group reads land in
+//    distinct banks.  In a chunk, lane group g = lane / 32 takes k in [64 g, 64 g + 64)
+//    and MFMA step s its 16 bytes [64 g + 16 s, +16); any per-lane k order is valid as
+//    long as A and B agree.  Double-buffered, one barrier per chunk.
+//  * B (sign bits, [N][K/8] rows): staged through LDS four chunks at a time, so each
+//    column contributes a 64-byte run (4 threads, 16 bytes each) instead of 16 bytes
+//    per chunk; rows of the LDS copy are padded to 72 bytes (conflict-free 8-byte
+//    reads).  Double-buffered per 4-chunk block, written two chunks before use.
+//  * Operands one step ahead: A fragments are read and B operands expanded for step
+//    s + 1 while step s's MFMAs run; loads run one to two chunks ahead.
+//  * Tails: every global access goes through a buffer resource; rows past M, columns
+//    past the tile and chunks past K or past the group's range read zero.
 //
 // Epilogue.  y = s_x (s_w acc + s_A sum_r W_A[n][r] s_B[r] t[m][r]).  The LoRA-up
 // product is a second, tiny contraction (rank 16) and runs on v_mfma_f32_32x32x16_bf16:
@@ -31,6 +39,10 @@
 // (h + m + l, each the truncation of the remainder), so the products are exact and
 // only fp32 accumulation rounds.  Its output layout equals the int32 accumulator's,
 // so the scale epilogue combines them register by register.
+//
+// One launch can carry two tile configurations over two column ranges (a main part
+// and a narrow tail), so that a width like 8512 = 16 x 512 + 320 fills the machine in
+// about one round instead of two.
 #include "device_common.h"
 
 namespace dfssm {
@@ -41,20 +53,61 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 namespace prefill {
 constexpr int kChunk = 128;            // k per main-loop chunk (64 per lane group)
+constexpr int kBlk = 4;                // chunks per staged block of sign bits
+constexpr int kLdA = kChunk + 16;      // LDS row stride of a code chunk (bytes)
+constexpr int kLdB = kBlk * 16 + 8;    // LDS row stride of a column's block of sign bits (bytes)
 constexpr int kLoadDead = 0x7ff00000;  // a load offset past every resource used here: reads zero
 constexpr int kRedBlocks = 8;          // accumulator blocks per split-K reduction phase
-constexpr int kColDead = 0x40000000;   // store offset added for columns past N: past the y resource
+constexpr int kColDead = 0x40000000;   // store offset added for columns past the range: past the y resource
+
+template <int MB_, int NB_, int KS_>
+struct Cfg {
+    static constexpr int MB = MB_, NB = NB_, KS = KS_;
+    static constexpr int WNW = 4 / KS;                       // waves along N
+    static constexpr int BM = 32 * MB, WN = 32 * NB, BN = WN * WNW;
+    static constexpr int GS = kWave * WNW;                   // threads of one K group
+    static constexpr int J = BM * 8 / (4 * GS);              // code pieces per thread per step
+    static constexpr int JB = BN * kBlk / GS;                // sign pieces per thread per block
+    static constexpr int kABytes = BM * kLdA, kBBytes = BN * kLdB;
+    static constexpr int kGroupBytes = 2 * kABytes + 2 * kBBytes;
+    static constexpr int kRedBytes = KS > 1 ? WNW * kRedBlocks * KS * 4 * kWave * 16 : 0;
+    // int32 [KS][BM] code sums, after both the chunk buffers and the split-K hand-over
+    // area that reuses them
+    static constexpr int kRowSumOff = KS * kGroupBytes > kRedBytes ? KS * kGroupBytes : kRedBytes;
+    static constexpr int kLdsBytes = kRowSumOff + KS * BM * 4;
+    static_assert(KS == 1 || KS == 2 || KS == 4, "4 waves split over K and N");
+    static_assert(J * 4 * GS == BM * 8, "code pieces split evenly over steps");
+    static_assert(JB * GS == BN * kBlk, "sign pieces split evenly over threads");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS");
+};
+
+// One part of a launch: a column range [n_begin, n_end) tiled by one configuration.
+struct Seg {
+    int tiles_m, tiles_n, n_begin, n_end;
+};
+
+struct Args {
+    const int8_t* x_q;
+    const float* s_x;
+    const uint8_t* w_bits;
+    const float* s_w;
+    const int8_t* w_a;
+    const float* s_a;
+    const float* s_b;
+    const int32_t* t;
+    float* y;
+    int32_t* acc_dbg;
+    int M, N, K, rank;
+};
 }  // namespace prefill
 
-// 4 sign bits -> 4 bytes of +-1 (bit i -> byte i).
-__device__ __forceinline__ uint32_t signs4(uint32_t nib) {
-    return perm(0u, 0x000001FFu, (nib * 0x00204081u) & 0x01010101u);
-}
+// 4 sign bits -> 4 bytes of 0/1 (bit i -> byte i).
+__device__ __forceinline__ uint32_t bits4(uint32_t nib) { return (nib * 0x00204081u) & 0x01010101u; }
 
-// Low 16 bits of w -> a 16-byte B operand of +-1 (bit i -> byte i).
-__device__ __forceinline__ v4i signs16(uint32_t w) {
-    return (v4i){(int)signs4(w & 0xFu), (int)signs4((w >> 4) & 0xFu), (int)signs4((w >> 8) & 0xFu),
-                 (int)signs4((w >> 12) & 0xFu)};
+// Low 16 bits of w -> a 16-byte B operand of 0/1 (bit i -> byte i).
+__device__ __forceinline__ v4i bits16(uint32_t w) {
+    return (v4i){(int)bits4(w & 0xFu), (int)bits4((w >> 4) & 0xFu), (int)bits4((w >> 8) & 0xFu),
+                 (int)bits4((w >> 12) & 0xFu)};
 }
 
 // Exact split of a finite fp32 value into three bf16 values, u = h + m + l: h keeps
@@ -76,82 +129,49 @@ __device__ __forceinline__ v8bf pack_bf16(const uint32_t (&b)[8]) {
     return __builtin_bit_cast(v8bf, w);
 }
 
-template <int MB, int NB, int KS, bool kDebug>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_prefill_kernel(
-    const int8_t* __restrict__ x_q, const float* __restrict__ s_x, int M, int N, int K,
-    const uint8_t* __restrict__ w_bits, const float* __restrict__ s_w, const int8_t* __restrict__ w_a,
-    const float* __restrict__ s_a, const float* __restrict__ s_b, const int32_t* __restrict__ t, int rank,
-    float* __restrict__ y, int32_t* __restrict__ acc_dbg, int tiles_m, int tiles_n) {
+// One output tile of configuration C over the column range of `seg`.
+template <class C, bool kDebug>
+__device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __restrict__ lds, int tile,
+                                             const prefill::Seg& seg) {
     using namespace prefill;
-    constexpr int WNW = 4 / KS;
-    constexpr int BM = 32 * MB, WN = 32 * NB, BN = WN * WNW;
-    static_assert(KS == 1 || KS == 2 || KS == 4, "4 waves split over K and N");
-    // LDS: per K group two chunk buffers of BM rows (row stride kLdA, padded so the
-    // 16 rows a 16-lane group reads land in distinct banks); the split-K reduction
-    // reuses the same bytes after the main loop.
-    constexpr int kLdA = kChunk + 16;
-    constexpr int kBufBytes = BM * kLdA;
-    constexpr int kMainBytes = KS * 2 * kBufBytes;
-    constexpr int kRedBytes = KS > 1 ? WNW * kRedBlocks * KS * 4 * kWave * 16 : 0;
-    __shared__ __align__(16) uint8_t lds[kMainBytes > kRedBytes ? kMainBytes : kRedBytes];
-    v4i* const red = reinterpret_cast<v4i*>(lds);
-    // staging: the WNW waves of a K group load its chunk, 16-byte pieces, 8 threads
-    // per 128-byte row segment (whole cache lines); J pieces per thread per step
-    constexpr int GS = kWave * WNW;
-    constexpr int J = BM * 8 / (4 * GS);
-    static_assert(J * 4 * GS == BM * 8, "chunk pieces split evenly over steps");
+    constexpr int MB = C::MB, NB = C::NB, KS = C::KS, WNW = C::WNW, BM = C::BM, WN = C::WN, BN = C::BN;
+    constexpr int GS = C::GS, J = C::J, JB = C::JB;
+    const int M = a.M, N = a.N, K = a.K;
 
-    // problem blockIdx.y of a dense batch
-    {
-        const int64_t p = blockIdx.y;
-        x_q += p * M * K;
-        s_x += p * M;
-        w_bits += p * N * (int64_t)(K / 8);
-        s_w += p * N;
-        y += p * M * N;
-        if (acc_dbg) acc_dbg += p * M * N;
-        if (rank != 0) {
-            w_a += p * N * kRank;
-            s_a += p * N;
-            s_b += p * kRank;
-            t += p * M * kRank;
-        }
-    }
-
-    // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous run
-    // of tiles (row-major), so the x_q rows and sign columns it reads stay in its L2.
-    const int T = tiles_m * tiles_n;
-    const int xcd = blockIdx.x % 8, q8 = T / 8, r8 = T % 8;
-    const int tile = xcd * q8 + min(xcd, r8) + (int)(blockIdx.x / 8);
-    const int tm = tile / tiles_n, tn = tile % tiles_n;
-
+    const int tm = tile / seg.tiles_n, tn = tile % seg.tiles_n;
     // wave index made visibly wave-uniform, so the per-wave buffer resources are scalar
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     const int lane = threadIdx.x % kWave;
     const int wn = wave % WNW, kq = wave / WNW;
     const int g = lane >> 5, l32 = lane & 31;
-    const int m0 = tm * BM, n0 = tn * BN + wn * WN;
+    const int tg = wn * kWave + lane;  // thread index within the K group
+    const int m0 = tm * BM;
+    const int n0g = seg.n_begin + tn * BN;  // first column of the workgroup
+    const int n0 = n0g + wn * WN;           // first column of this wave
     const int RB = K / 8;
     // (readfirstlane: the clamps compile to VALU min/max, whose results the resource
     // builder would otherwise treat as per-lane)
     const int rows = __builtin_amdgcn_readfirstlane(min(M - m0, BM));
-    const int cols = __builtin_amdgcn_readfirstlane(max(0, min(N - n0, WN)));
+    const int cols_g = __builtin_amdgcn_readfirstlane(max(0, min(seg.n_end - n0g, BN)));
+    const int cols = __builtin_amdgcn_readfirstlane(max(0, min(seg.n_end - n0, WN)));
 
-    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(x_q + (int64_t)m0 * K, (uint32_t)(rows * K));
-    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(w_bits + (int64_t)min(n0, N) * RB, (uint32_t)(cols * RB));
-    int b_off[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) b_off[nb] = 32 * nb + l32 < cols ? (32 * nb + l32) * RB : kLoadDead;
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(a.x_q + (int64_t)m0 * K, (uint32_t)(rows * K));
+    const __amdgpu_buffer_rsrc_t b_rsrc =
+        make_rsrc(a.w_bits + (int64_t)min(n0g, N) * RB, (uint32_t)(cols_g * RB));
 
-    // every wave runs the same number of chunks (the barriers pair up); chunks past
-    // its K range read zeros
+    // every wave runs the same number of chunks (the barriers pair up), a multiple of
+    // the sign-bit block; chunks past its K range read zeros
     const int nch = (K + kChunk - 1) / kChunk;
-    const int per = (nch + KS - 1) / KS;
+    const int per = ((nch + KS - 1) / KS + kBlk - 1) / kBlk * kBlk;
     const int c_begin = kq * per, c_end = min(nch, c_begin + per);
+    const int nblk = per / kBlk;
 
-    // staging pieces of this thread: step s, slot j -> row (s J + j) GS / 8 + tg / 8,
-    // bytes [16 p, 16 p + 16) of the row's chunk segment
-    const int tg = wn * kWave + lane, p16 = 16 * (tg & 7);
+    uint8_t* const abuf = lds + kq * C::kGroupBytes;  // 2 x kABytes, this K group's
+    uint8_t* const bbuf = abuf + 2 * C::kABytes;       // 2 x kBBytes
+    int32_t* const rowsum = reinterpret_cast<int32_t*>(lds + C::kRowSumOff);
+
+    // code staging: step s, slot j -> row (s J + j) GS / 8 + tg / 8, bytes [16 p, +16)
+    const int p16 = 16 * (tg & 7);
     int st_goff[4][J], st_loff[4][J];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -161,88 +181,120 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             st_goff[s][j] = r < rows ? r * K + p16 : kLoadDead;
             st_loff[s][j] = r * kLdA + p16;
         }
-    uint8_t* const abase = lds + kq * 2 * kBufBytes;
+    // sign staging: slot i -> group column (tg / 4) + (GS / 4) i, chunk (tg & 3) of the block
+    int bs_goff[JB], bs_loff[JB];
+#pragma unroll
+    for (int i = 0; i < JB; ++i) {
+        const int c = (tg >> 2) + (GS / 4) * i;
+        bs_goff[i] = c < cols_g ? c * RB + 16 * (tg & 3) : kLoadDead;
+        bs_loff[i] = c * kLdB + 16 * (tg & 3);
+    }
 
-    // piece (s, j) of chunk c (zero past the wave's chunk range or past K)
     auto st_load = [&](int c, int s, int j) -> v4i {
         const int k = c * kChunk;
         const bool live = c < c_end && k + p16 < K;
         return __builtin_bit_cast(
             v4i, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, live ? st_goff[s][j] + k : kLoadDead, 0, 0));
     };
+    // sign bits of block b (chunks c_begin + 4 b .. + 3), slot i: 16 bytes of its chunk
+    auto bs_load = [&](int b, int i) -> v4i {
+        const int c0 = c_begin + kBlk * b;
+        const bool live = b < nblk && c0 + (tg & 3) < c_end;
+        return __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, live ? bs_goff[i] + 16 * c0 : kLoadDead, 0, 0));
+    };
     // A operand of step s, row block mb: row 32 mb + l32, bytes [64 g + 16 s, +16)
     auto a_frag = [&](int buf, int s, int mb) -> v4i {
-        return *reinterpret_cast<const v4i*>(abase + buf * kBufBytes + (32 * mb + l32) * kLdA + 64 * g + 16 * s);
+        return *reinterpret_cast<const v4i*>(abuf + buf * C::kABytes + (32 * mb + l32) * kLdA + 64 * g + 16 * s);
     };
-    // 64 sign bits of column nb for chunk c: k in [c kChunk + 64 g, +64)
-    auto b_load = [&](int c, int nb) -> v2u {
-        const int k = c * kChunk + 64 * g;
-        const bool live = c < c_end && k < K;
-        return __builtin_bit_cast(
-            v2u, __builtin_amdgcn_raw_buffer_load_b64(b_rsrc, live ? b_off[nb] + k / 8 : kLoadDead, 0, 0));
+    // this lane's 64 sign bits of column block nb, chunk q of block buffer bb: k in
+    // [c kChunk + 64 g, +64)
+    auto b_bits = [&](int bb, int q, int nb) -> v2u {
+        return *reinterpret_cast<const v2u*>(bbuf + bb * C::kBBytes + (wn * WN + 32 * nb + l32) * kLdB + 16 * q +
+                                             8 * g);
     };
-    // B operand of step s from a chunk's 64 sign bits
-    auto b_op = [](const v2u& bits, int s) -> v4i {
-        return signs16((s < 2 ? bits.x : bits.y) >> (16 * (s & 1)));
-    };
+    auto b_op = [](const v2u& bits, int s) -> v4i { return bits16((s < 2 ? bits.x : bits.y) >> (16 * (s & 1))); };
 
     v16i acc[MB][NB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = (v16i){};
+    int rsum[4][J];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int j = 0; j < J; ++j) rsum[s][j] = 0;
 
-    // prologue: chunk c_begin into LDS buffer 0, chunk c_begin + 1 into the staging
-    // registers, sign bits of both chunks, the first A and B operands
-    v4i stage[4][J];
+    // ---- prologue: chunk 0 and sign block 0 into LDS; chunk 1 in flight ----
+    v4i stage[4][J], bst[JB];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int j = 0; j < J; ++j) stage[s][j] = st_load(c_begin, s, j);
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int j = 0; j < J; ++j) *reinterpret_cast<v4i*>(abase + st_loff[s][j]) = stage[s][j];
+    for (int i = 0; i < JB; ++i) bst[i] = bs_load(0, i);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int j = 0; j < J; ++j) stage[s][j] = st_load(c_begin + 1, s, j);
-    v2u bb0[NB], bb1[NB];
+        for (int j = 0; j < J; ++j) {
+            *reinterpret_cast<v4i*>(abuf + st_loff[s][j]) = stage[s][j];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        bb0[nb] = b_load(c_begin, nb);
-        bb1[nb] = b_load(c_begin + 1, nb);
-    }
+            for (int w = 0; w < 4; ++w) rsum[s][j] = byte_sum((uint32_t)stage[s][j][w], rsum[s][j]);
+            stage[s][j] = st_load(c_begin + 1, s, j);
+        }
+#pragma unroll
+    for (int i = 0; i < JB; ++i) *reinterpret_cast<v4i*>(bbuf + bs_loff[i]) = bst[i];
     lds_barrier();
-    // A and B operands are fetched / expanded one step ahead (double buffers), so each
-    // step's LDS reads and VALU work are independent of its MFMAs and interleave.
     v4i afr[2][MB], bop[2][NB];
+    v2u bits0[NB], bits1[NB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) afr[0][mb] = a_frag(0, 0, mb);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) bop[0][nb] = b_op(bb0[nb], 0);
+    for (int nb = 0; nb < NB; ++nb) {
+        bits0[nb] = b_bits(0, 0, nb);
+        bop[0][nb] = b_op(bits0[nb], 0);
+    }
     // Drain the prologue's loads here, once: the wait the loop header needs is the
     // worst case over its entry and back edge, and an entry with loads still in
     // flight would make every iteration wait for nearly all of its own loads.
     __builtin_amdgcn_s_waitcnt(0);
 
-    // One chunk c, read from LDS buffer `cur`: per step s, store staged piece s of
-    // chunk c + 1 into the other buffer and reload it with chunk c + 2, fetch the next
-    // step's A operands, run the step's MFMAs while expanding the next B operands.
-    // The one barrier per chunk sits in step 3, after the last store of chunk c + 1
-    // and before its first operand read; every read of `cur` was issued before it.
-    auto chunk = [&](int c, int cur, v2u (&bb)[NB], const v2u (&bn)[NB]) {
-        const int nxt = cur ^ 1;
+    // One chunk: the q-th of sign block b, code buffer q & 1, sign bits bc (the next
+    // chunk's go to bn).  Per step s: store staged piece s of the next chunk into the
+    // other code buffer and reload it two chunks ahead; fetch the next step's A
+    // operands; run this step's MFMAs while expanding the next B operands.  Step 1
+    // reads the next chunk's sign bits.  Chunk 0 of block b loads block b + 1's sign
+    // bits and chunk 2 stores them, a chunk before chunk 3 first reads them.  The one
+    // barrier per chunk sits in step 3, after the last store and before the first read
+    // of the next chunk; every read of the current buffers was issued before it.
+    auto chunk = [&](int b, int q, const v2u (&bc)[NB], v2u (&bn)[NB]) {
+        const int c = c_begin + kBlk * b + q;
+        const int cur = q & 1, nxt = cur ^ 1;
+        const int bb_cur = b & 1;
+        if (q == 0) {
+#pragma unroll
+            for (int i = 0; i < JB; ++i) bst[i] = bs_load(b + 1, i);
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                *reinterpret_cast<v4i*>(abase + nxt * kBufBytes + st_loff[s][j]) = stage[s][j];
+                *reinterpret_cast<v4i*>(abuf + nxt * C::kABytes + st_loff[s][j]) = stage[s][j];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) rsum[s][j] = byte_sum((uint32_t)stage[s][j][w], rsum[s][j]);
                 stage[s][j] = st_load(c + 2, s, j);
             }
-            if (s == 3) {
+            if (s == 1) {
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) bb[nb] = b_load(c + 2, nb);
+                for (int nb = 0; nb < NB; ++nb) bn[nb] = q < 3 ? b_bits(bb_cur, q + 1, nb) : b_bits(bb_cur ^ 1, 0, nb);
+            }
+            if (s == 3) {
+                if (q == 2) {
+#pragma unroll
+                    for (int i = 0; i < JB; ++i)
+                        *reinterpret_cast<v4i*>(bbuf + (bb_cur ^ 1) * C::kBBytes + bs_loff[i]) = bst[i];
+                }
                 lds_barrier();
             }
 #pragma unroll
@@ -253,30 +305,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 for (int mb = 0; mb < MB; ++mb)
                     acc[mb][nb] =
                         __builtin_amdgcn_mfma_i32_32x32x32_i8(afr[s & 1][mb], bop[s & 1][nb], acc[mb][nb], 0, 0, 0);
-                bop[(s + 1) & 1][nb] = s < 3 ? b_op(bb[nb], s + 1) : b_op(bn[nb], 0);
+                bop[(s + 1) & 1][nb] = s < 3 ? b_op(bc[nb], s + 1) : b_op(bn[nb], 0);
             }
             // one scheduling region per step, so loads stay where they are issued
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    for (int i = 0; i < per; i += 2) {
-        chunk(c_begin + i, 0, bb0, bb1);
-        chunk(c_begin + i + 1, 1, bb1, bb0);
+    for (int b = 0; b < nblk; ++b) {
+        chunk(b, 0, bits0, bits1);
+        chunk(b, 1, bits1, bits0);
+        chunk(b, 2, bits0, bits1);
+        chunk(b, 3, bits1, bits0);
     }
-    lds_barrier();  // the reduction below reuses the chunk buffers
 
-    // Split-K: the KS waves of one column group hold partial sums of the same tile.
-    // Block b = nb * MB + mb belongs to wave kq = b % KS; the others hand theirs over
+    // token code sums of this K group: the 8 threads of a row hold one 16-byte column
+    // of it each
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            int v = rsum[s][j];
+            v += __shfl_xor(v, 1, kWave);
+            v += __shfl_xor(v, 2, kWave);
+            v += __shfl_xor(v, 4, kWave);
+            if ((tg & 7) == 0) rowsum[kq * BM + (s * J + j) * (GS / 8) + (tg >> 3)] = v;
+        }
+    lds_barrier();  // row sums published; the reduction below reuses the chunk buffers
+
+    // Split-K: the KS groups of one column group hold partial sums of the same tile.
+    // Block b = nb * MB + mb belongs to group kq = b % KS; the others hand theirs over
     // through LDS, kRedBlocks blocks per phase.  Every wave runs every barrier.
     constexpr int NBLK = MB * NB;
     if constexpr (KS > 1) {
+        v4i* const red = reinterpret_cast<v4i*>(lds);
 #pragma unroll
         for (int p0 = 0; p0 < NBLK; p0 += kRedBlocks) {
 #pragma unroll
-            for (int b = p0; b < NBLK && b < p0 + kRedBlocks; ++b) {
-                const int mb = b % MB, nb = b / MB;
-                if (kq != b % KS) {
-                    const int slot = ((wn * kRedBlocks + (b - p0)) * KS + kq) * 4;
+            for (int bI = p0; bI < NBLK && bI < p0 + kRedBlocks; ++bI) {
+                const int mb = bI % MB, nb = bI / MB;
+                if (kq != bI % KS) {
+                    const int slot = ((wn * kRedBlocks + (bI - p0)) * KS + kq) * 4;
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         red[(slot + j) * kWave + lane] = (v4i){acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1],
@@ -285,13 +353,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
             lds_barrier();
 #pragma unroll
-            for (int b = p0; b < NBLK && b < p0 + kRedBlocks; ++b) {
-                const int mb = b % MB, nb = b / MB;
-                if (kq == b % KS) {
+            for (int bI = p0; bI < NBLK && bI < p0 + kRedBlocks; ++bI) {
+                const int mb = bI % MB, nb = bI / MB;
+                if (kq == bI % KS) {
 #pragma unroll
                     for (int q = 0; q < KS; ++q) {
-                        if (q == b % KS) continue;
-                        const int slot = ((wn * kRedBlocks + (b - p0)) * KS + q) * 4;
+                        if (q == bI % KS) continue;
+                        const int slot = ((wn * kRedBlocks + (bI - p0)) * KS + q) * 4;
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const v4i v = red[(slot + j) * kWave + lane];
@@ -308,21 +376,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // ---- epilogue: LoRA-up on bf16 MFMA, scales, stores ----
     // Every load and store below goes through a resource sized to this tile, so no
     // element needs a branch: rows past M fall past the y resource by construction,
-    // columns past N get kColDead added, and a missing LoRA reads as zeros.
-    const bool lora = rank != 0;
+    // columns past the range get kColDead added, and a missing LoRA reads as zeros.
+    const bool lora = a.rank != 0;
     const int N4 = N * 4;
-    const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(y + (int64_t)m0 * N, (uint32_t)(rows * N4));
+    const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(a.y + (int64_t)m0 * N, (uint32_t)(rows * N4));
     const __amdgpu_buffer_rsrc_t d_rsrc =
-        make_rsrc(kDebug ? acc_dbg + (int64_t)m0 * N : acc_dbg, kDebug ? (uint32_t)(rows * N4) : 0u);
-    const __amdgpu_buffer_rsrc_t sx_rsrc = make_rsrc(s_x + m0, (uint32_t)(rows * 4));
+        make_rsrc(kDebug ? a.acc_dbg + (int64_t)m0 * N : a.acc_dbg, kDebug ? (uint32_t)(rows * N4) : 0u);
+    const __amdgpu_buffer_rsrc_t sx_rsrc = make_rsrc(a.s_x + m0, (uint32_t)(rows * 4));
     const int ncl = min(n0, N);
-    const __amdgpu_buffer_rsrc_t sw_rsrc = make_rsrc(s_w + ncl, (uint32_t)(cols * 4));
-    const __amdgpu_buffer_rsrc_t sa_rsrc = make_rsrc(lora ? s_a + ncl : s_a, lora ? (uint32_t)(cols * 4) : 0u);
+    const __amdgpu_buffer_rsrc_t sw_rsrc = make_rsrc(a.s_w + ncl, (uint32_t)(cols * 4));
+    const __amdgpu_buffer_rsrc_t sa_rsrc = make_rsrc(lora ? a.s_a + ncl : a.s_a, lora ? (uint32_t)(cols * 4) : 0u);
     const __amdgpu_buffer_rsrc_t wa_rsrc =
-        make_rsrc(lora ? w_a + (int64_t)ncl * kRank : w_a, lora ? (uint32_t)(cols * kRank) : 0u);
+        make_rsrc(lora ? a.w_a + (int64_t)ncl * kRank : a.w_a, lora ? (uint32_t)(cols * kRank) : 0u);
     const __amdgpu_buffer_rsrc_t t_rsrc =
-        make_rsrc(lora ? t + (int64_t)m0 * kRank : t, lora ? (uint32_t)(rows * kRank * 4) : 0u);
-    const __amdgpu_buffer_rsrc_t sb_rsrc = make_rsrc(s_b, lora ? (uint32_t)(kRank * 4) : 0u);
+        make_rsrc(lora ? a.t + (int64_t)m0 * kRank : a.t, lora ? (uint32_t)(rows * kRank * 4) : 0u);
+    const __amdgpu_buffer_rsrc_t sb_rsrc = make_rsrc(a.s_b, lora ? (uint32_t)(kRank * 4) : 0u);
 
     // per column block: this lane's column n0 + 32 nb + l32
     float sw[NB], sa[NB];
@@ -364,14 +432,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int nb = 0; nb < NB; ++nb) any = any || kq == (nb * MB + mb) % KS;
         if (!any) continue;
 
-        // s_x of this lane's 16 output rows 32 mb + 8 (v / 4) + 4 g + v % 4
+        // s_x and the code sum R of this lane's 16 output rows 32 mb + 8 (v / 4) + 4 g + v % 4
         float sx[16];
+        int rs[16];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 32 * mb + 8 * j + 4 * g;
             const v4u v = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(sx_rsrc, r * 4, 0, 0));
+            v4i rt = *reinterpret_cast<const v4i*>(rowsum + r);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sx[4 * j + i] = __uint_as_float(v[i]);
+            for (int q = 1; q < KS; ++q) rt += *reinterpret_cast<const v4i*>(rowsum + q * BM + r);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sx[4 * j + i] = __uint_as_float(v[i]);
+                rs[4 * j + i] = rt[i];
+            }
         }
         // u = s_B t for token row 32 mb + l32, ranks 8 g .. 8 g + 7, as three bf16 parts
         v8bf uh, um, ul;
@@ -405,58 +480,167 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int v = 0; v < 16; ++v) {
                 // row 32 mb + 8 (v / 4) + 4 g + v % 4 (past `rows`: past the resource)
                 const int off = base + (8 * (v / 4) + (v % 4)) * N4;
-                const int32_t a = acc[mb][nb][v];
+                const int32_t acc_pm = 2 * acc[mb][nb][v] - rs[v];  // the +-1 sum
                 // without LoRA, sa = lo = 0 and the fma returns s_w acc unchanged
-                const float inner = fmaf(sa[nb], lo[v], sw[nb] * (float)a);
+                const float inner = fmaf(sa[nb], lo[v], sw[nb] * (float)acc_pm);
                 store_f32(sx[v] * inner, y_rsrc, off);
-                if constexpr (kDebug) store_i32(a, d_rsrc, off);
+                if constexpr (kDebug) store_i32(acc_pm, d_rsrc, off);
             }
         }
     }
 }
 
+// Problem blockIdx.y of a dense batch; blocks [0, T0) run configuration C0 over seg0,
+// the rest C1 over seg1.  Segment 0's tiles are dealt to the 8 XCDs in contiguous runs
+// (workgroups go to XCDs round-robin), so the code rows and sign columns one XCD reads
+// stay in its L2.
+template <class C0, class C1, bool kDebug>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_prefill_kernel(
+    prefill::Args a, prefill::Seg seg0, prefill::Seg seg1) {
+    constexpr int kLds = C0::kLdsBytes > C1::kLdsBytes ? C0::kLdsBytes : C1::kLdsBytes;
+    __shared__ __align__(16) uint8_t lds[kLds];
+    {
+        const int64_t p = blockIdx.y;
+        const int64_t M = a.M, N = a.N, K = a.K;
+        a.x_q += p * M * K;
+        a.s_x += p * M;
+        a.w_bits += p * N * (K / 8);
+        a.s_w += p * N;
+        a.y += p * M * N;
+        if (kDebug) a.acc_dbg += p * M * N;
+        if (a.rank != 0) {
+            a.w_a += p * N * kRank;
+            a.s_a += p * N;
+            a.s_b += p * kRank;
+            a.t += p * M * kRank;
+        }
+    }
+    const int T0 = seg0.tiles_m * seg0.tiles_n;
+    const int b = blockIdx.x;
+    if (b < T0) {
+        const int xcd = b % 8, q8 = T0 / 8, r8 = T0 % 8;
+        const int tile = xcd * q8 + min(xcd, r8) + b / 8;
+        prefill_tile<C0, kDebug>(a, lds, tile, seg0);
+    } else {
+        prefill_tile<C1, kDebug>(a, lds, b - T0, seg1);
+    }
+}
+
 namespace {
 
-struct PrefillCfg {
-    int mb, nb, ks;
-};
+using prefill::Cfg;
+using prefill::Seg;
 
-constexpr PrefillCfg kPrefillCfgs[] = {{4, 4, 1}, {4, 4, 2}, {4, 4, 4}};
+// Tile configurations (row blocks, column blocks per wave, K groups):
+using C441 = Cfg<4, 4, 1>;  // 128 x 512, wide N
+using C422 = Cfg<4, 2, 2>;  // 128 x 128, split-K by 2
+using C412 = Cfg<4, 1, 2>;  // 128 x 64, split-K by 2 (narrow parts)
+
+struct CfgInfo {
+    int bm, bn, ks, wave_cols;
+};
+constexpr CfgInfo kCfgs[] = {{128, 512, 1, 128}, {128, 128, 2, 64}, {128, 64, 2, 32}};
+constexpr int kNumCfgs = 3;
 constexpr int kNumCUs = 256;
 
-template <int MB, int NB, int KS>
-hipError_t launch_cfg(const int8_t* x_q, const float* s_x, int M, int N, int K, const uint8_t* w_bits,
-                      const float* s_w, const int8_t* w_a, const float* s_a, const float* s_b, const int32_t* t,
-                      int rank, float* y, int32_t* acc_dbg, int64_t batch, hipStream_t stream) {
-    const int BM = 32 * MB, BN = 32 * NB * (4 / KS);
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)batch);
-    if (acc_dbg) {
-        gemm_prefill_kernel<MB, NB, KS, true><<<grid, 256, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a,
-                                                                        s_b, t, rank, y, acc_dbg, tiles_m, tiles_n);
+struct Plan {
+    int main_cfg, tail_cfg;  // indices into kCfgs; tail_cfg < 0: no tail
+    int n_split;             // columns [0, n_split) main, [n_split, N) tail
+};
+
+int64_t tiles_of(int cfg, int64_t M, int64_t n_cols) {
+    const CfgInfo& c = kCfgs[cfg];
+    return ((M + c.bm - 1) / c.bm) * ((n_cols + c.bn - 1) / c.bn);
+}
+
+// Modelled time of one part, in units of a 128 x 128 x 128 MFMA step of one wave:
+// rounds of one-workgroup-per-CU tiles times the steps of one wave (a chunk count
+// rounded up to the 4-chunk sign block), 10 % extra for the split-K hand-over.
+double part_cost(int cfg, int64_t M, int64_t n_cols, int64_t K, int64_t batch, int64_t* wgs_out) {
+    const CfgInfo& c = kCfgs[cfg];
+    const int64_t wgs = tiles_of(cfg, M, n_cols) * batch;
+    if (wgs_out) *wgs_out = wgs;
+    const int64_t rounds = (wgs + kNumCUs - 1) / kNumCUs;
+    const int64_t nch = (K + 127) / 128;
+    const int64_t per = ((nch + c.ks - 1) / c.ks + 3) / 4 * 4;
+    return (double)rounds * (double)per * (c.wave_cols / 128.0) * (c.ks > 1 ? 1.1 : 1.0);
+}
+
+Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t batch, int force, int force_tail) {
+    if (force >= 0 && force < kNumCfgs) {
+        // pinned: whole tiles of `force`, the rest (if any) on `force_tail` when that
+        // is a narrower configuration
+        const int64_t n_main = N / kCfgs[force].bn * kCfgs[force].bn;
+        if (force_tail >= 0 && force_tail < kNumCfgs && kCfgs[force_tail].bn < kCfgs[force].bn && n_main > 0 &&
+            n_main < N)
+            return Plan{force, force_tail, (int)n_main};
+        return Plan{force, -1, (int)N};
+    }
+    Plan best{0, -1, (int)N};
+    double best_cost = 1e300;
+    for (int mc = 0; mc < kNumCfgs; ++mc) {
+        int64_t wgs_main = 0;
+        const double whole = part_cost(mc, M, N, K, batch, &wgs_main);
+        if (whole < best_cost) {
+            best_cost = whole;
+            best = Plan{mc, -1, (int)N};
+        }
+        // whole main tiles, the remainder on a narrower configuration in the same
+        // launch: its workgroups take the CUs the main part leaves free, then the CUs
+        // that finish first
+        const int64_t n_main = N / kCfgs[mc].bn * kCfgs[mc].bn;
+        if (n_main == 0 || n_main == N) continue;
+        for (int tc = 0; tc < kNumCfgs; ++tc) {
+            if (kCfgs[tc].bn >= kCfgs[mc].bn) continue;
+            int64_t wm = 0, wt = 0;
+            const double cm = part_cost(mc, M, n_main, K, batch, &wm);
+            const double ct = part_cost(tc, M, N - n_main, K, batch, &wt);
+            const int64_t free_cus = (kNumCUs - wm % kNumCUs) % kNumCUs;
+            const double cost = wt <= free_cus ? (cm > ct ? cm : ct) : cm + ct;
+            if (cost < best_cost) {
+                best_cost = cost;
+                best = Plan{mc, tc, (int)n_main};
+            }
+        }
+    }
+    return best;
+}
+
+template <class C0, class C1>
+hipError_t launch2(const prefill::Args& a, const Seg& s0, const Seg& s1, int64_t batch, hipStream_t stream) {
+    const int64_t blocks = (int64_t)s0.tiles_m * s0.tiles_n + (int64_t)s1.tiles_m * s1.tiles_n;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)blocks, (unsigned)batch);
+    if (a.acc_dbg) {
+        gemm_prefill_kernel<C0, C1, true><<<grid, 256, 0, stream>>>(a, s0, s1);
     } else {
-        gemm_prefill_kernel<MB, NB, KS, false><<<grid, 256, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a,
-                                                                         s_b, t, rank, y, acc_dbg, tiles_m, tiles_n);
+        gemm_prefill_kernel<C0, C1, false><<<grid, 256, 0, stream>>>(a, s0, s1);
     }
     return hipGetLastError();
 }
 
-// Modelled time of a configuration: whole rounds of 256 one-workgroup-per-CU tiles,
-// times the MFMA steps per wave, plus the split-K hand-over.
-double cfg_cost(const PrefillCfg& c, int64_t M, int64_t N, int64_t K, int64_t batch) {
-    const int64_t BM = 32 * c.mb, BN = 32 * c.nb * (4 / c.ks);
-    const int64_t wgs = ((M + BM - 1) / BM) * ((N + BN - 1) / BN) * batch;
-    const int64_t rounds = (wgs + kNumCUs - 1) / kNumCUs;
-    const int64_t nch = (K + 127) / 128;
-    const int64_t steps = (int64_t)c.mb * c.nb * ((nch + c.ks - 1) / c.ks);
-    return (double)rounds * (double)steps * (c.ks > 1 ? 1.15 : 1.0);
+template <class C>
+Seg make_seg(int64_t M, int n_begin, int n_end) {
+    return Seg{(int)((M + C::BM - 1) / C::BM), (n_end - n_begin + C::BN - 1) / C::BN, n_begin, n_end};
+}
+
+template <class C0>
+hipError_t launch_main(const prefill::Args& a, const Plan& p, int64_t batch, hipStream_t stream) {
+    const Seg s0 = make_seg<C0>(a.M, 0, p.n_split);
+    const Seg none{0, 0, a.N, a.N};
+    switch (p.tail_cfg) {
+        case 1: return launch2<C0, C422>(a, s0, make_seg<C422>(a.M, p.n_split, a.N), batch, stream);
+        case 2: return launch2<C0, C412>(a, s0, make_seg<C412>(a.M, p.n_split, a.N), batch, stream);
+        default: return launch2<C0, C0>(a, s0, none, batch, stream);
+    }
 }
 
 }  // namespace
 
-// Tile configurations the prefill kernel can take, for tests that pin one
-// (index into kPrefillCfgs; -1 = pick by the cost model).
-int prefill_num_cfgs() { return (int)(sizeof(kPrefillCfgs) / sizeof(kPrefillCfgs[0])); }
+// Tile configurations the prefill kernel can be pinned to by tests (index; -1 = pick
+// by the cost model; a tail configuration applies to the columns past the last whole
+// main tile).
+int prefill_num_cfgs() { return kNumCfgs; }
 
 // The prefill kernel needs K % 64 == 0 (whole 64-k lane-group slices) and per-tile
 // byte offsets of y below 2^30 (128 rows x N x 4 bytes, plus kColDead below 2^31).
@@ -468,28 +652,13 @@ bool prefill_supported(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm_prefill(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                                const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
                                const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                               int64_t batch, int force_cfg, hipStream_t stream) {
-    int best = 0;
-    if (force_cfg >= 0 && force_cfg < prefill_num_cfgs()) {
-        best = force_cfg;
-    } else {
-        double best_cost = 0.0;
-        for (int i = 0; i < prefill_num_cfgs(); ++i) {
-            const double c = cfg_cost(kPrefillCfgs[i], M, N, K, batch);
-            if (i == 0 || c < best_cost) {
-                best = i;
-                best_cost = c;
-            }
-        }
-    }
-    const PrefillCfg c = kPrefillCfgs[best];
-    const int64_t BM = 32 * c.mb, BN = 32 * c.nb * (4 / c.ks);
-    if (((M + BM - 1) / BM) * ((N + BN - 1) / BN) > 0x7fffffffLL) return hipErrorInvalidValue;
-    const int m = (int)M, n = (int)N, k = (int)K;
-    switch (best) {
-        case 0: return launch_cfg<4, 4, 1>(x_q, s_x, m, n, k, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, stream);
-        case 1: return launch_cfg<4, 4, 2>(x_q, s_x, m, n, k, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, stream);
-        default: return launch_cfg<4, 4, 4>(x_q, s_x, m, n, k, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, stream);
+                               int64_t batch, int force_cfg, int force_tail, hipStream_t stream) {
+    const prefill::Args a{x_q, s_x, w_bits, s_w, w_a, s_a, s_b, t, y, acc_dbg, (int)M, (int)N, (int)K, rank};
+    const Plan p = plan_for(M, N, K, batch, force_cfg, force_tail);
+    switch (p.main_cfg) {
+        case 0: return launch_main<C441>(a, p, batch, stream);
+        case 1: return launch_main<C422>(a, p, batch, stream);
+        default: return launch_main<C412>(a, p, batch, stream);
     }
 }
 
