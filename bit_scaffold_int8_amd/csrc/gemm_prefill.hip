@@ -60,23 +60,25 @@ constexpr int kLoadDead = 0x7ff00000;  // a load offset past every resource used
 constexpr int kRedBlocks = 8;          // accumulator blocks per split-K reduction phase
 constexpr int kColDead = 0x40000000;   // store offset added for columns past the range: past the y resource
 
-template <int MB_, int NB_, int KS_>
+template <int MB_, int NB_, int KS_, int NW_ = 4>
 struct Cfg {
-    static constexpr int MB = MB_, NB = NB_, KS = KS_;
-    static constexpr int WNW = 4 / KS;                       // waves along N
+    static constexpr int MB = MB_, NB = NB_, KS = KS_, NW = NW_;
+    static constexpr int WNW = NW / KS;                      // waves along N
     static constexpr int BM = 32 * MB, WN = 32 * NB, BN = WN * WNW;
     static constexpr int GS = kWave * WNW;                   // threads of one K group
-    static constexpr int J = BM * 8 / (4 * GS);              // code pieces per thread per step
+    static constexpr int P = BM * 8 / GS;                    // code pieces per thread per chunk
     static constexpr int JB = BN * kBlk / GS;                // sign pieces per thread per block
     static constexpr int kABytes = BM * kLdA, kBBytes = BN * kLdB;
     static constexpr int kGroupBytes = 2 * kABytes + 2 * kBBytes;
-    static constexpr int kRedBytes = KS > 1 ? WNW * kRedBlocks * KS * 4 * kWave * 16 : 0;
+    static constexpr int RBLK = MB * NB < kRedBlocks ? MB * NB : kRedBlocks;  // blocks per hand-over phase
+    static constexpr int kRedBytes = KS > 1 ? WNW * RBLK * KS * 4 * kWave * 16 : 0;
     // int32 [KS][BM] code sums, after both the chunk buffers and the split-K hand-over
     // area that reuses them
     static constexpr int kRowSumOff = KS * kGroupBytes > kRedBytes ? KS * kGroupBytes : kRedBytes;
     static constexpr int kLdsBytes = kRowSumOff + KS * BM * 4;
-    static_assert(KS == 1 || KS == 2 || KS == 4, "4 waves split over K and N");
-    static_assert(J * 4 * GS == BM * 8, "code pieces split evenly over steps");
+    static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
+    static_assert(KS == 1 || KS == 2 || KS == 4, "waves split over K and N");
+    static_assert(P * GS == BM * 8 && (P % 4 == 0 || 4 % P == 0), "code pieces split evenly over steps");
     static_assert(JB * GS == BN * kBlk, "sign pieces split evenly over threads");
     static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
@@ -135,7 +137,9 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
                                              const prefill::Seg& seg) {
     using namespace prefill;
     constexpr int MB = C::MB, NB = C::NB, KS = C::KS, WNW = C::WNW, BM = C::BM, WN = C::WN, BN = C::BN;
-    constexpr int GS = C::GS, J = C::J, JB = C::JB;
+    constexpr int GS = C::GS, P = C::P, JB = C::JB, RBLK = C::RBLK;
+    // code piece j is staged in step st_step(j) of a chunk
+    auto st_step = [](int j) { return j * 4 / P; };
     const int M = a.M, N = a.N, K = a.K;
 
     const int tm = tile / seg.tiles_n, tn = tile % seg.tiles_n;
@@ -170,17 +174,15 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     uint8_t* const bbuf = abuf + 2 * C::kABytes;       // 2 x kBBytes
     int32_t* const rowsum = reinterpret_cast<int32_t*>(lds + C::kRowSumOff);
 
-    // code staging: step s, slot j -> row (s J + j) GS / 8 + tg / 8, bytes [16 p, +16)
+    // code staging: piece j -> row j GS / 8 + tg / 8, bytes [16 p, +16)
     const int p16 = 16 * (tg & 7);
-    int st_goff[4][J], st_loff[4][J];
+    int st_goff[P], st_loff[P];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int r = (s * J + j) * (GS / 8) + (tg >> 3);
-            st_goff[s][j] = r < rows ? r * K + p16 : kLoadDead;
-            st_loff[s][j] = r * kLdA + p16;
-        }
+    for (int j = 0; j < P; ++j) {
+        const int r = j * (GS / 8) + (tg >> 3);
+        st_goff[j] = r < rows ? r * K + p16 : kLoadDead;
+        st_loff[j] = r * kLdA + p16;
+    }
     // sign staging: slot i -> group column (tg / 4) + (GS / 4) i, chunk (tg & 3) of the block
     int bs_goff[JB], bs_loff[JB];
 #pragma unroll
@@ -190,11 +192,11 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
         bs_loff[i] = c * kLdB + 16 * (tg & 3);
     }
 
-    auto st_load = [&](int c, int s, int j) -> v4i {
+    auto st_load = [&](int c, int j) -> v4i {
         const int k = c * kChunk;
         const bool live = c < c_end && k + p16 < K;
         return __builtin_bit_cast(
-            v4i, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, live ? st_goff[s][j] + k : kLoadDead, 0, 0));
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, live ? st_goff[j] + k : kLoadDead, 0, 0));
     };
     // sign bits of block b (chunks c_begin + 4 b .. + 3), slot i: 16 bytes of its chunk
     auto bs_load = [&](int b, int i) -> v4i {
@@ -220,29 +222,23 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = (v16i){};
-    int rsum[4][J];
+    int rsum[P];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int j = 0; j < J; ++j) rsum[s][j] = 0;
+    for (int j = 0; j < P; ++j) rsum[j] = 0;
 
     // ---- prologue: chunk 0 and sign block 0 into LDS; chunk 1 in flight ----
-    v4i stage[4][J], bst[JB];
+    v4i stage[P], bst[JB];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int j = 0; j < J; ++j) stage[s][j] = st_load(c_begin, s, j);
+    for (int j = 0; j < P; ++j) stage[j] = st_load(c_begin, j);
 #pragma unroll
     for (int i = 0; i < JB; ++i) bst[i] = bs_load(0, i);
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int j = 0; j < P; ++j) {
+        *reinterpret_cast<v4i*>(abuf + st_loff[j]) = stage[j];
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            *reinterpret_cast<v4i*>(abuf + st_loff[s][j]) = stage[s][j];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) rsum[s][j] = byte_sum((uint32_t)stage[s][j][w], rsum[s][j]);
-            stage[s][j] = st_load(c_begin + 1, s, j);
-        }
+        for (int w = 0; w < 4; ++w) rsum[j] = byte_sum((uint32_t)stage[j][w], rsum[j]);
+        stage[j] = st_load(c_begin + 1, j);
+    }
 #pragma unroll
     for (int i = 0; i < JB; ++i) *reinterpret_cast<v4i*>(bbuf + bs_loff[i]) = bst[i];
     lds_barrier();
@@ -279,11 +275,12 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
-            for (int j = 0; j < J; ++j) {
-                *reinterpret_cast<v4i*>(abuf + nxt * C::kABytes + st_loff[s][j]) = stage[s][j];
+            for (int j = 0; j < P; ++j) {
+                if (st_step(j) != s) continue;
+                *reinterpret_cast<v4i*>(abuf + nxt * C::kABytes + st_loff[j]) = stage[j];
 #pragma unroll
-                for (int w = 0; w < 4; ++w) rsum[s][j] = byte_sum((uint32_t)stage[s][j][w], rsum[s][j]);
-                stage[s][j] = st_load(c + 2, s, j);
+                for (int w = 0; w < 4; ++w) rsum[j] = byte_sum((uint32_t)stage[j][w], rsum[j]);
+                stage[j] = st_load(c + 2, j);
             }
             if (s == 1) {
 #pragma unroll
@@ -321,30 +318,28 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     // token code sums of this K group: the 8 threads of a row hold one 16-byte column
     // of it each
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            int v = rsum[s][j];
-            v += __shfl_xor(v, 1, kWave);
-            v += __shfl_xor(v, 2, kWave);
-            v += __shfl_xor(v, 4, kWave);
-            if ((tg & 7) == 0) rowsum[kq * BM + (s * J + j) * (GS / 8) + (tg >> 3)] = v;
-        }
+    for (int j = 0; j < P; ++j) {
+        int v = rsum[j];
+        v += __shfl_xor(v, 1, kWave);
+        v += __shfl_xor(v, 2, kWave);
+        v += __shfl_xor(v, 4, kWave);
+        if ((tg & 7) == 0) rowsum[kq * BM + j * (GS / 8) + (tg >> 3)] = v;
+    }
     lds_barrier();  // row sums published; the reduction below reuses the chunk buffers
 
     // Split-K: the KS groups of one column group hold partial sums of the same tile.
     // Block b = nb * MB + mb belongs to group kq = b % KS; the others hand theirs over
-    // through LDS, kRedBlocks blocks per phase.  Every wave runs every barrier.
+    // through LDS, RBLK blocks per phase.  Every wave runs every barrier.
     constexpr int NBLK = MB * NB;
     if constexpr (KS > 1) {
         v4i* const red = reinterpret_cast<v4i*>(lds);
 #pragma unroll
-        for (int p0 = 0; p0 < NBLK; p0 += kRedBlocks) {
+        for (int p0 = 0; p0 < NBLK; p0 += RBLK) {
 #pragma unroll
-            for (int bI = p0; bI < NBLK && bI < p0 + kRedBlocks; ++bI) {
+            for (int bI = p0; bI < NBLK && bI < p0 + RBLK; ++bI) {
                 const int mb = bI % MB, nb = bI / MB;
                 if (kq != bI % KS) {
-                    const int slot = ((wn * kRedBlocks + (bI - p0)) * KS + kq) * 4;
+                    const int slot = ((wn * RBLK + (bI - p0)) * KS + kq) * 4;
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         red[(slot + j) * kWave + lane] = (v4i){acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1],
@@ -353,13 +348,13 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
             }
             lds_barrier();
 #pragma unroll
-            for (int bI = p0; bI < NBLK && bI < p0 + kRedBlocks; ++bI) {
+            for (int bI = p0; bI < NBLK && bI < p0 + RBLK; ++bI) {
                 const int mb = bI % MB, nb = bI / MB;
                 if (kq == bI % KS) {
 #pragma unroll
                     for (int q = 0; q < KS; ++q) {
                         if (q == bI % KS) continue;
-                        const int slot = ((wn * kRedBlocks + (bI - p0)) * KS + q) * 4;
+                        const int slot = ((wn * RBLK + (bI - p0)) * KS + q) * 4;
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const v4i v = red[(slot + j) * kWave + lane];
@@ -495,8 +490,9 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
 // (workgroups go to XCDs round-robin), so the code rows and sign columns one XCD reads
 // stay in its L2.
 template <class C0, class C1, bool kDebug>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_prefill_kernel(
-    prefill::Args a, prefill::Seg seg0, prefill::Seg seg1) {
+__global__ __launch_bounds__(C0::NW * kWave) __attribute__((amdgpu_waves_per_eu(C0::NW / 4, C0::NW / 4))) void
+gemm_prefill_kernel(prefill::Args a, prefill::Seg seg0, prefill::Seg seg1) {
+    static_assert(C0::NW == C1::NW, "both parts of a launch use the same workgroup size");
     constexpr int kLds = C0::kLdsBytes > C1::kLdsBytes ? C0::kLdsBytes : C1::kLdsBytes;
     __shared__ __align__(16) uint8_t lds[kLds];
     {
@@ -531,16 +527,22 @@ namespace {
 using prefill::Cfg;
 using prefill::Seg;
 
-// Tile configurations (row blocks, column blocks per wave, K groups):
-using C441 = Cfg<4, 4, 1>;  // 128 x 512, wide N
-using C422 = Cfg<4, 2, 2>;  // 128 x 128, split-K by 2
-using C412 = Cfg<4, 1, 2>;  // 128 x 64, split-K by 2 (narrow parts)
+// Tile configurations (row blocks, column blocks per wave, K groups, waves):
+using C441 = Cfg<4, 4, 1>;     // 128 x 512, wide N
+using C422 = Cfg<4, 2, 2>;     // 128 x 128, split-K by 2
+using C412 = Cfg<4, 1, 2>;     // 128 x 64, split-K by 2 (narrow parts)
+using C4218 = Cfg<4, 2, 1, 8>;  // 128 x 512, two waves per SIMD
+using C4128 = Cfg<4, 1, 2, 8>;  // 128 x 128, split-K by 2, two waves per SIMD
+using C2128 = Cfg<2, 1, 2, 8>;  // 64 x 128, split-K by 2, two waves per SIMD (narrow parts)
+using C2148 = Cfg<2, 1, 4, 8>;  // 64 x 64, split-K by 4, two waves per SIMD (narrow parts)
 
 struct CfgInfo {
-    int bm, bn, ks, wave_cols;
+    int bm, bn, ks, nw, wave_cols;
 };
-constexpr CfgInfo kCfgs[] = {{128, 512, 1, 128}, {128, 128, 2, 64}, {128, 64, 2, 32}};
-constexpr int kNumCfgs = 3;
+constexpr CfgInfo kCfgs[] = {{128, 512, 1, 4, 128}, {128, 128, 2, 4, 64}, {128, 64, 2, 4, 32},
+                             {128, 512, 1, 8, 64},  {128, 128, 2, 8, 32}, {64, 128, 2, 8, 32},
+                             {64, 64, 4, 8, 32}};
+constexpr int kNumCfgs = 7;
 constexpr int kNumCUs = 256;
 
 struct Plan {
@@ -553,9 +555,11 @@ int64_t tiles_of(int cfg, int64_t M, int64_t n_cols) {
     return ((M + c.bm - 1) / c.bm) * ((n_cols + c.bn - 1) / c.bn);
 }
 
-// Modelled time of one part, in units of a 128 x 128 x 128 MFMA step of one wave:
-// rounds of one-workgroup-per-CU tiles times the steps of one wave (a chunk count
-// rounded up to the 4-chunk sign block), 10 % extra for the split-K hand-over.
+// Modelled time of one part, in units of a 128 x 128 x 128 MFMA step of one SIMD:
+// rounds of one-workgroup-per-CU tiles times the steps of one SIMD (a chunk count
+// rounded up to the 4-chunk sign block), 10 % extra for the split-K hand-over, 15 %
+// less with two waves per SIMD (measured: their stalls overlap), and 60 % more for
+// 64-row tiles (half the MFMAs per expanded sign operand).
 double part_cost(int cfg, int64_t M, int64_t n_cols, int64_t K, int64_t batch, int64_t* wgs_out) {
     const CfgInfo& c = kCfgs[cfg];
     const int64_t wgs = tiles_of(cfg, M, n_cols) * batch;
@@ -563,7 +567,8 @@ double part_cost(int cfg, int64_t M, int64_t n_cols, int64_t K, int64_t batch, i
     const int64_t rounds = (wgs + kNumCUs - 1) / kNumCUs;
     const int64_t nch = (K + 127) / 128;
     const int64_t per = ((nch + c.ks - 1) / c.ks + 3) / 4 * 4;
-    return (double)rounds * (double)per * (c.wave_cols / 128.0) * (c.ks > 1 ? 1.1 : 1.0);
+    return (double)rounds * (double)per * (c.wave_cols * c.nw / 4 / 128.0) * (c.bm / 128.0) *
+           (c.ks > 1 ? 1.1 : 1.0) * (c.nw == 8 ? 0.85 : 1.0) * (c.bm < 128 ? 1.6 : 1.0);
 }
 
 Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t batch, int force, int force_tail) {
@@ -571,8 +576,8 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t batch, int force, int for
         // pinned: whole tiles of `force`, the rest (if any) on `force_tail` when that
         // is a narrower configuration
         const int64_t n_main = N / kCfgs[force].bn * kCfgs[force].bn;
-        if (force_tail >= 0 && force_tail < kNumCfgs && kCfgs[force_tail].bn < kCfgs[force].bn && n_main > 0 &&
-            n_main < N)
+        if (force_tail >= 0 && force_tail < kNumCfgs && kCfgs[force_tail].bn < kCfgs[force].bn &&
+            kCfgs[force_tail].nw == kCfgs[force].nw && n_main > 0 && n_main < N)
             return Plan{force, force_tail, (int)n_main};
         return Plan{force, -1, (int)N};
     }
@@ -591,7 +596,7 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t batch, int force, int for
         const int64_t n_main = N / kCfgs[mc].bn * kCfgs[mc].bn;
         if (n_main == 0 || n_main == N) continue;
         for (int tc = 0; tc < kNumCfgs; ++tc) {
-            if (kCfgs[tc].bn >= kCfgs[mc].bn) continue;
+            if (kCfgs[tc].bn >= kCfgs[mc].bn || kCfgs[tc].nw != kCfgs[mc].nw) continue;
             int64_t wm = 0, wt = 0;
             const double cm = part_cost(mc, M, n_main, K, batch, &wm);
             const double ct = part_cost(tc, M, N - n_main, K, batch, &wt);
@@ -612,9 +617,9 @@ hipError_t launch2(const prefill::Args& a, const Seg& s0, const Seg& s1, int64_t
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks, (unsigned)batch);
     if (a.acc_dbg) {
-        gemm_prefill_kernel<C0, C1, true><<<grid, 256, 0, stream>>>(a, s0, s1);
+        gemm_prefill_kernel<C0, C1, true><<<grid, C0::NW * kWave, 0, stream>>>(a, s0, s1);
     } else {
-        gemm_prefill_kernel<C0, C1, false><<<grid, 256, 0, stream>>>(a, s0, s1);
+        gemm_prefill_kernel<C0, C1, false><<<grid, C0::NW * kWave, 0, stream>>>(a, s0, s1);
     }
     return hipGetLastError();
 }
@@ -624,15 +629,16 @@ Seg make_seg(int64_t M, int n_begin, int n_end) {
     return Seg{(int)((M + C::BM - 1) / C::BM), (n_end - n_begin + C::BN - 1) / C::BN, n_begin, n_end};
 }
 
-template <class C0>
-hipError_t launch_main(const prefill::Args& a, const Plan& p, int64_t batch, hipStream_t stream) {
+template <class C0, class T0, class T1>
+hipError_t launch_main(const prefill::Args& a, const Plan& p, int tail0, int tail1, int64_t batch,
+                       hipStream_t stream) {
     const Seg s0 = make_seg<C0>(a.M, 0, p.n_split);
     const Seg none{0, 0, a.N, a.N};
-    switch (p.tail_cfg) {
-        case 1: return launch2<C0, C422>(a, s0, make_seg<C422>(a.M, p.n_split, a.N), batch, stream);
-        case 2: return launch2<C0, C412>(a, s0, make_seg<C412>(a.M, p.n_split, a.N), batch, stream);
-        default: return launch2<C0, C0>(a, s0, none, batch, stream);
-    }
+    if (p.tail_cfg >= 0 && p.tail_cfg == tail0)
+        return launch2<C0, T0>(a, s0, make_seg<T0>(a.M, p.n_split, a.N), batch, stream);
+    if (p.tail_cfg >= 0 && p.tail_cfg == tail1)
+        return launch2<C0, T1>(a, s0, make_seg<T1>(a.M, p.n_split, a.N), batch, stream);
+    return launch2<C0, C0>(a, s0, none, batch, stream);
 }
 
 }  // namespace
@@ -656,9 +662,13 @@ hipError_t launch_gemm_prefill(const int8_t* x_q, const float* s_x, int64_t M, i
     const prefill::Args a{x_q, s_x, w_bits, s_w, w_a, s_a, s_b, t, y, acc_dbg, (int)M, (int)N, (int)K, rank};
     const Plan p = plan_for(M, N, K, batch, force_cfg, force_tail);
     switch (p.main_cfg) {
-        case 0: return launch_main<C441>(a, p, batch, stream);
-        case 1: return launch_main<C422>(a, p, batch, stream);
-        default: return launch_main<C412>(a, p, batch, stream);
+        case 0: return launch_main<C441, C422, C412>(a, p, 1, 2, batch, stream);
+        case 1: return launch_main<C422, C412, C412>(a, p, 2, 2, batch, stream);
+        case 2: return launch_main<C412, C412, C412>(a, p, -1, -1, batch, stream);
+        case 3: return launch_main<C4218, C2128, C2148>(a, p, 5, 6, batch, stream);
+        case 4: return launch_main<C4128, C2128, C2148>(a, p, 5, 6, batch, stream);
+        case 5: return launch_main<C2128, C2148, C2148>(a, p, 6, 6, batch, stream);
+        default: return launch_main<C2148, C2148, C2148>(a, p, -1, -1, batch, stream);
     }
 }
 
