@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kLoraWaves * kWave) void lora_down_kernel(
     // D[4g + v][i]: token 4g+v, rank i
 #pragma unroll
     for (int v = 0; v < 4; ++v) part[wave][4 * g + v][i] = acc[v];
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x < 256) {
         const int tok = threadIdx.x >> 4, r = threadIdx.x & 15;
         int32_t s = 0;

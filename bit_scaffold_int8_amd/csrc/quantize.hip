@@ -72,7 +72,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
     v = wave_max(v);
     const int wave = threadIdx.x / kWave;
     if ((threadIdx.x & (kWave - 1)) == 0) red[wave] = v;
-    __syncthreads();
+    lds_barrier();
     float m = red[0];
 #pragma unroll
     for (int w = 1; w < kQuantThreads / kWave; ++w) m = fmaxf(m, red[w]);
@@ -187,13 +187,16 @@ namespace dfssm {
 constexpr int kQLWaves = 8;
 constexpr int kQLThreads = kQLWaves * kWave;
 constexpr int64_t kQLLdsBytes = 65536 - 1024;  // codes; the rest of 64 KiB holds the t tile
-constexpr int kQLRegVec = 16;  // float4 per lane kept in registers (K <= 4096 at a wave per row)
-constexpr int kQLPre = 8;      // W_B fragments per wave fetched ahead (covers K <= 4096)
+// Template parameters: NV float4 of a row per lane kept in registers (a row longer than
+// the waves sharing it hold is read twice), NP W_B fragments per wave fetched ahead.
+// The launch picks the smallest that cover the row, so short rows leave registers for
+// more resident groups.
 
 __device__ __forceinline__ float absmax4(float4 v) {
     return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
+template <int kQLRegVec, int kQLPre>
 __global__ __launch_bounds__(kQLThreads) void quantize_lora_down_kernel(
     const float* __restrict__ x, int64_t M, int64_t K, const int8_t* __restrict__ w_b, int rank,
     int8_t* __restrict__ x_q, float* __restrict__ s_x, int32_t* __restrict__ t, int tokens_per_group) {
@@ -266,10 +269,10 @@ __global__ __launch_bounds__(kQLThreads) void quantize_lora_down_kernel(
         }
         amax = wave_max(amax);
         if (lane == 0) amax_part[wave] = amax;
-        __syncthreads();
+        lds_barrier();
         const int w0 = (wave / wpr) * wpr;
         for (int w = 0; w < wpr; ++w) amax = fmaxf(amax, amax_part[w0 + w]);
-        __syncthreads();  // amax_part is rewritten by the next pass
+        lds_barrier();  // amax_part is rewritten by the next pass
         if (live) {
             const RowScale rs = row_scale(amax);
             if (lane == 0 && sub == 0) s_x[m] = amax == 0.0f ? 0.0f : rs.s;
@@ -309,7 +312,7 @@ __global__ __launch_bounds__(kQLThreads) void quantize_lora_down_kernel(
         }
     }
     if (rank == 0) return;
-    __syncthreads();
+    lds_barrier();
 
     // ---- phase 2: t tile = codes (16 tokens, LDS) x W_B^T (16 ranks, global)
     const uint8_t* arow = lds_q + (int64_t)i * K;
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(kQLThreads) void quantize_lora_down_kernel(
     // give the exact sum in any order
 #pragma unroll
     for (int v = 0; v < 4; ++v) atomicAdd(&tsum[4 * g + v][i], acc[v]);
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x < 256) {
         const int tok = threadIdx.x >> 4, r = threadIdx.x & 15;
         if (tok < rows) t[(m0 + tok) * kRank + r] = tsum[tok][r];
@@ -352,11 +355,35 @@ int quantize_lora_tokens_per_group(int64_t K) {
 
 hipError_t launch_quantize_lora_down(const float* x, int64_t M, int64_t K, const int8_t* w_b, int rank,
                                      int8_t* x_q, float* s_x, int32_t* t, int64_t batch, hipStream_t stream) {
-    const int tpg = quantize_lora_tokens_per_group(K);
+    int tpg = quantize_lora_tokens_per_group(K);
     if (tpg <= 0 || K % 4 != 0) return hipErrorInvalidValue;
+    // Many tokens: fewer per group, so that there are about two groups per CU (each
+    // group's rows are one latency-bound pass; W_B, read by every group, stays in L2).
+    const int64_t want = (M * batch + 511) / 512;
+    if (want < tpg) tpg = (int)(want < 1 ? 1 : want);
+    // registers: the float4 per lane of a full group's rows (waves per row as the
+    // kernel picks them), and W_B steps per wave
+    auto wpr_of = [](int64_t rows) -> int64_t { return rows >= 8 ? 1 : (rows >= 4 ? 2 : (rows >= 2 ? 4 : 8)); };
+    auto nv_of = [&](int64_t g) -> int64_t {
+        const int64_t rows = M < g ? M : g, wpr = wpr_of(rows);
+        return (K / 4 + wpr * kWave - 1) / (wpr * kWave);
+    };
+    // rows that need more than 4 float4 per lane cost the second resident group per
+    // CU anyway: then take twice the rows per group (one wave per row, all rows' loads
+    // in flight at once, one group per CU)
+    if (M * batch >= 1024 && nv_of(tpg) > 4 && 2 * tpg <= quantize_lora_tokens_per_group(K)) tpg = 2 * tpg;
+    const int64_t nv = nv_of(tpg);
+    const int64_t np = ((K + 63) / 64 + kQLWaves - 1) / kQLWaves;
     const dim3 grid((unsigned)((M + tpg - 1) / tpg), (unsigned)batch);
     const size_t lds = (size_t)tpg * (size_t)K;
-    quantize_lora_down_kernel<<<grid, kQLThreads, lds, stream>>>(x, M, K, w_b, rank, x_q, s_x, t, tpg);
+#define DFSSM_QL(NV, NP) \
+    quantize_lora_down_kernel<NV, NP><<<grid, kQLThreads, lds, stream>>>(x, M, K, w_b, rank, x_q, s_x, t, tpg)
+    if (nv <= 4 && np <= 4) DFSSM_QL(4, 4);
+    else if (nv <= 4) DFSSM_QL(4, 8);
+    else if (nv <= 8 && np <= 4) DFSSM_QL(8, 4);
+    else if (nv <= 8) DFSSM_QL(8, 8);
+    else DFSSM_QL(16, 8);
+#undef DFSSM_QL
     return hipGetLastError();
 }
 
