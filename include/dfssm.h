@@ -124,8 +124,12 @@ dfssm_status dfssm_quantize_lora_down_strided_batched(const float* x, int64_t M,
  *   acc_dbg      optional int32 [M][N]: when not NULL, also receives the exact
  *                scaffold accumulators sum_k w x_q (verification aid)
  * Requires M, N >= 1, K >= 8, K % 8 == 0, K <= 131072.  M <= 16 (with K <= 16384)
- * runs the bandwidth-bound decode kernel, otherwise the int8 MFMA kernel; either
- * way one kernel launch.
+ * runs the bandwidth-bound decode kernel, otherwise an int8 MFMA kernel (tile
+ * configuration chosen by a cost model of the shape; K % 64 != 0 takes a generic
+ * fallback kernel); either way one kernel launch.  For tests and tuning, the
+ * environment variable DFSSM_PREFILL_CFG pins the MFMA kernel's tile configuration
+ * (0, 1, ...; -2 = the generic kernel) and DFSSM_PREFILL_TAIL a narrower one for the
+ * columns past the pinned one's last whole tile; results are the same either way.
  */
 dfssm_status dfssm_scaffold_lora_gemm(const int8_t* x_q, const float* s_x,
                                       int64_t M, int64_t N, int64_t K,
