@@ -31,8 +31,10 @@
 
 namespace dfssm {
 
-// Rows one workgroup owns at most (their epilogue operands live in LDS).
-constexpr int kGemvRowsPerWG = 1024;
+// Rows one workgroup owns at most (their epilogue operands live in LDS): 2048 for the
+// 8-wave, 4-tile-stage shape that large batches run (one group per 2048-row problem),
+// 1024 otherwise, which keeps more of the smaller groups resident per CU.
+constexpr int gemv_rows_cap(int W, int T) { return (W >= 8 && T >= 4) ? 2048 : 1024; }
 
 // One lane group = 16 lanes; one chunk = 16 packed bytes = 128 k of one row.
 // W waves split K; C chunks per lane; T row tiles (16 rows each) per stage.
@@ -50,13 +52,14 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     constexpr int kTokStride = W * kWave / (T * 16);
 
     // per-row epilogue operands of every row this group owns, staged once at setup
-    __shared__ uint4 wa_lds[kGemvRowsPerWG];
-    __shared__ float sa_lds[kGemvRowsPerWG];
-    __shared__ float sw_lds[kGemvRowsPerWG];
-    // the stage's scaffold sums, added into by every wave (exact integer adds commute).
-    // Row stride 20 words keeps the adds of one instruction (rows 4g+v, tokens i) on
-    // distinct banks.
-    __shared__ int32_t red[1][T * 16][20];
+    constexpr int kRowsCap = gemv_rows_cap(W, T);
+    __shared__ uint4 wa_lds[kRowsCap];
+    __shared__ float sa_lds[kRowsCap];
+    __shared__ float sw_lds[kRowsCap];
+    // the stage's scaffold sums, added into by every wave (exact integer adds commute),
+    // double-buffered by stage parity so one barrier per stage suffices.  Row stride 20
+    // words keeps the adds of one instruction (rows 4g+v, tokens i) on distinct banks.
+    __shared__ int32_t red[2][T * 16][20];
     __shared__ int32_t xs_part[W][kWave];
     __shared__ int32_t xsum[16];
     __shared__ float u[16][kRank];
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     }
     if (threadIdx.x < 16) sxs[threadIdx.x] = sxv;
     xs_part[wave][lane] = xpart;
-    for (int e = threadIdx.x; e < T * 16 * 20; e += W * kWave) (&red[0][0][0])[e] = 0;
+    for (int e = threadIdx.x; e < 2 * T * 16 * 20; e += W * kWave) (&red[0][0][0])[e] = 0;
     lds_barrier();
     if (threadIdx.x < 16) {
         int32_t s = 0;
@@ -301,14 +304,17 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
                 store_f32(sxs[tok] * inner, y_rsrc, off);
             }
         }
-        lds_barrier();  // the sums are re-added into by the next stage
+        // No second barrier: the next stage adds into the other buffer, and this one is
+        // added into again only after the next stage's barrier, which every wave reaches
+        // after finishing this epilogue.
     };
 
     // three stages per trip so the register buffers rotate by name
     for (int64_t st = st_begin; st < st_end; st += 3) {
-        run_stage(st, s0, s2, 0);
-        run_stage(st + 1, s1, s0, 0);
-        run_stage(st + 2, s2, s1, 0);
+        const int rb = (int)((st - st_begin) & 1);
+        run_stage(st, s0, s2, rb);
+        run_stage(st + 1, s1, s0, rb ^ 1);
+        run_stage(st + 2, s2, s1, rb);
     }
 }
 
@@ -319,12 +325,15 @@ static hipError_t launch_gemv_wct(bool fast, const int8_t* x_q, const float* s_x
                                   int64_t batch, hipStream_t stream) {
     const int64_t num_tiles = (N + 15) / 16;
     const int64_t num_stages = (num_tiles + T - 1) / T;
-    // ~8 groups per CU in flight overall; beyond that, groups take more stages,
-    // which amortizes their activation setup
-    const int64_t target_wgs = 2048;
+    // Large batches: about one resident round of groups (two 512-thread groups per CU
+    // when a group is 8 waves), each over as many rows as it can hold, so the setup is
+    // paid once per group and no second round trails.  Otherwise ~8 groups per CU.
+    const int64_t resident_wgs = 256 * (W >= 8 ? 2 : 16 / W);
+    const int64_t target_wgs = batch * num_stages >= 4 * resident_wgs ? resident_wgs : 2048;
     const int64_t per_problem = (target_wgs + batch - 1) / batch;
     int stages_per_wg = (int)((num_stages + per_problem - 1) / per_problem);
-    if (stages_per_wg * T * 16 > kGemvRowsPerWG) stages_per_wg = kGemvRowsPerWG / (T * 16);
+    constexpr int kRowsCap = gemv_rows_cap(W, T);
+    if (stages_per_wg * T * 16 > kRowsCap) stages_per_wg = kRowsCap / (T * 16);
     const dim3 grid((unsigned)((num_stages + stages_per_wg - 1) / stages_per_wg), (unsigned)batch);
     if (fast) {
         gemv_kernel<W, C, T, true><<<grid, W * kWave, 0, stream>>>(

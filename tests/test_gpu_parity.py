@@ -213,6 +213,28 @@ def test_strided_batched_matches_oracle_per_problem(torch_cuda, B, M, N, K):
         _assert_y(dp.y[b].cpu().numpy(), y_ref, D, f"batch {b}")
 
 
+@pytest.mark.parametrize("B,M,N,K", [(512, 1, 2048, 4096), (200, 3, 2000, 4096), (300, 16, 1024, 2048)])
+def test_large_batches_one_group_round(torch_cuda, B, M, N, K):
+    # batches large enough that the decode kernel gives each group a whole problem (or
+    # an even share of one) in a single resident round: the benchmark's launch (512
+    # out_proj copies), ragged rows with an uneven split, and 16 tokens on 4-wave groups
+    import torch
+    from bit_scaffold_int8_amd.runner import DeviceProjections
+    probs = si.make_copies(M, N, K, 2, seed=B + N + K, copies=B)
+    dp = DeviceProjections.from_problems(probs, with_acc=True)
+    dp.forward()
+    torch.cuda.synchronize()
+    acc_all, y_all, t_all = dp.acc_dbg.cpu().numpy(), dp.y.cpu().numpy(), dp.t.cpu().numpy()
+    for b, prob in enumerate(probs):
+        xq_ref, sx_ref = oracle.quantize_act(prob.x)
+        y_ref, acc_ref, t_ref = oracle.scaffold_lora_gemm(xq_ref, sx_ref, prob.P, prob.s_w, prob.W_A, prob.s_A,
+                                                          prob.W_B, prob.s_B, nthreads=16)
+        assert np.array_equal(t_all[b], t_ref), b
+        assert np.array_equal(acc_all[b], acc_ref), b
+        D = _magnitude(sx_ref, prob.s_w, acc_ref, prob.s_A, prob.W_A, prob.s_B, t_ref)
+        _assert_y(y_all[b], y_ref, D, f"batch {b}")
+
+
 def test_gemm_without_debug_output_gives_same_y(torch_cuda):
     import torch
     from bit_scaffold_int8_amd.runner import DeviceProjections
