@@ -196,7 +196,9 @@ __device__ __forceinline__ float absmax4(float4 v) {
     return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
-template <int kQLRegVec, int kQLPre>
+// kRows16: K % 16 == 0, so a 16-byte W_B chunk lies wholly inside its row or wholly
+// past it, and every global load of the kernel is a branch-free buffer load.
+template <int kQLRegVec, int kQLPre, bool kRows16>
 __global__ __launch_bounds__(kQLThreads) void quantize_lora_down_kernel(
     const float* __restrict__ x, int64_t M, int64_t K, const int8_t* __restrict__ w_b, int rank,
     int8_t* __restrict__ x_q, float* __restrict__ s_x, int32_t* __restrict__ t, int tokens_per_group) {
@@ -214,29 +216,42 @@ __global__ __launch_bounds__(kQLThreads) void quantize_lora_down_kernel(
     }
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));  // uniform
     const int64_t m0 = (int64_t)blockIdx.x * tokens_per_group;
     const int rows = (int)((M - m0) < tokens_per_group ? (M - m0) : tokens_per_group);
     const int64_t K4 = K / 4;
     if (threadIdx.x < 256) tsum[threadIdx.x >> 4][threadIdx.x & 15] = 0;
+    // loads past a buffer's range read zero; a dead offset lies past every range
+    constexpr int kLoadDead = 0x7ff00000;
 
-    // W_B does not depend on x: its first fragments are fetched before the row loads
+    // W_B does not depend on x: its first fragments are fetched right after the row
+    // loads, so the absmax waits for the row only and the W_B stream overlaps the
+    // quantization
     const int i = lane & 15, g = lane >> 4;
     const uint8_t* brow = reinterpret_cast<const uint8_t*>(w_b) + (int64_t)i * K;
     const int64_t steps = (K + 63) / 64;
     const bool rows16 = (K % 16) == 0;  // 16-byte aligned rows in LDS and in W_B
+    // the problem's W_B (rank 0: an empty range, so every load reads zero)
+    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(w_b, rank != 0 ? (uint32_t)(kRank * K) : 0u);
     auto load_b = [&](int64_t st) -> uint4 {
         const int64_t off = st * 64 + 16 * g;
-        if (rank == 0 || st >= steps || off >= K) return make_uint4(0u, 0u, 0u, 0u);
-        if (rows16 && off + 16 <= K) return *reinterpret_cast<const uint4*>(brow + off);
-        uint32_t bw[4] = {0u, 0u, 0u, 0u};
-        for (int e = 0; e < 4; ++e)
-            if (off + 4 * e < K) bw[e] = *reinterpret_cast<const uint32_t*>(brow + off + 4 * e);
-        return make_uint4(bw[0], bw[1], bw[2], bw[3]);
+        if constexpr (kRows16) {
+            const int o = off < K ? (int)(i * K + off) : kLoadDead;
+            const v4i v = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, o, 0, 0);
+            return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+        } else {
+            if (rank == 0 || st >= steps || off >= K) return make_uint4(0u, 0u, 0u, 0u);
+            uint32_t bw[4] = {0u, 0u, 0u, 0u};
+            for (int e = 0; e < 4; ++e)
+                if (off + 4 * e < K) bw[e] = *reinterpret_cast<const uint32_t*>(brow + off + 4 * e);
+            return make_uint4(bw[0], bw[1], bw[2], bw[3]);
+        }
     };
     uint4 bpre[kQLPre];
+    auto prefetch_b = [&]() {
 #pragma unroll
-    for (int u = 0; u < kQLPre; ++u) bpre[u] = load_b(wave + (int64_t)u * kQLWaves);
+        for (int u = 0; u < kQLPre; ++u) bpre[u] = load_b(wave + (int64_t)u * kQLWaves);
+    };
 
     // ---- phase 1: quantize the group's rows.  Few rows (decode): several waves
     // share a row and combine their absmax through LDS; many rows: a wave per row.
@@ -255,17 +270,25 @@ __global__ __launch_bounds__(kQLThreads) void quantize_lora_down_kernel(
         const int64_t lbase = (int64_t)sub * kWave + lane;
         float4 v[kQLRegVec];
         float amax = 0.0f;
-        if (live) {
-            if (in_regs) {
+        if (in_regs) {
+            // the row through a buffer resource (a dead row has an empty range): no
+            // branch around the loads, so the absmax below waits for them alone
+            const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(x + m * K, live ? (uint32_t)(K * 4) : 0u);
 #pragma unroll
-                for (int e = 0; e < kQLRegVec; ++e) {
-                    const int64_t idx = lbase + (int64_t)e * lstride;
-                    v[e] = idx < K4 ? row4[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
-                    amax = fmaxf(amax, absmax4(v[e]));
-                }
-            } else {
-                for (int64_t idx = lbase; idx < K4; idx += lstride) amax = fmaxf(amax, absmax4(row4[idx]));
+            for (int e = 0; e < kQLRegVec; ++e) {
+                const v4f t4 = __builtin_bit_cast(
+                    v4f, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (int)((lbase + (int64_t)e * lstride) * 16), 0, 0));
+                v[e] = make_float4(t4[0], t4[1], t4[2], t4[3]);
             }
+        } else if (live) {
+            for (int64_t idx = lbase; idx < K4; idx += lstride) amax = fmaxf(amax, absmax4(row4[idx]));
+        }
+        // (re-issued on every pass: identical values, L2 hits after the first, and a
+        // load on every path keeps the wait below partial)
+        prefetch_b();
+        if (in_regs) {
+#pragma unroll
+            for (int e = 0; e < kQLRegVec; ++e) amax = fmaxf(amax, absmax4(v[e]));
         }
         amax = wave_max(amax);
         if (lane == 0) amax_part[wave] = amax;
@@ -277,27 +300,18 @@ __global__ __launch_bounds__(kQLThreads) void quantize_lora_down_kernel(
             const RowScale rs = row_scale(amax);
             if (lane == 0 && sub == 0) s_x[m] = amax == 0.0f ? 0.0f : rs.s;
             if (in_regs) {
-                uint64_t near = 0;  // bit 4e+c: element c of float4 e needs the exact quotient
 #pragma unroll
                 for (int e = 0; e < kQLRegVec; ++e) {
                     const int64_t idx = lbase + (int64_t)e * lstride;
                     if (idx < K4) {
                         uint32_t n4 = 0;
-                        const uint32_t q = amax == 0.0f ? 0u : fast_code4(v[e], rs.inv, n4);
+                        uint32_t q = amax == 0.0f ? 0u : fast_code4(v[e], rs.inv, n4);
+                        // rare: a code within reach of a rounding tie is redone with the
+                        // IEEE quotient, from the values still in registers
+                        if (amax != 0.0f && (!rs.fast || n4)) q = exact_code4(v[e], rs.s);
                         q4[idx] = q;
                         l4[idx] = q;
-                        if (amax != 0.0f) near |= (uint64_t)(rs.fast ? n4 : 0xFu) << (4 * e);
                     }
-                }
-                int8_t* qb = x_q + m * K;
-                int8_t* lb = reinterpret_cast<int8_t*>(lds_q) + (int64_t)r * K;
-                while (near) {  // rare: redo flagged elements exactly (same thread, same bytes)
-                    const int bit = __builtin_ctzll(near);
-                    near &= near - 1;
-                    const int64_t k = 4 * (lbase + (int64_t)(bit >> 2) * lstride) + (bit & 3);
-                    const int8_t c = exact_code(x[m * K + k], rs.s);
-                    qb[k] = c;
-                    lb[k] = c;
                 }
             } else {
                 for (int64_t idx = lbase; idx < K4; idx += lstride) {
@@ -376,8 +390,15 @@ hipError_t launch_quantize_lora_down(const float* x, int64_t M, int64_t K, const
     const int64_t np = ((K + 63) / 64 + kQLWaves - 1) / kQLWaves;
     const dim3 grid((unsigned)((M + tpg - 1) / tpg), (unsigned)batch);
     const size_t lds = (size_t)tpg * (size_t)K;
-#define DFSSM_QL(NV, NP) \
-    quantize_lora_down_kernel<NV, NP><<<grid, kQLThreads, lds, stream>>>(x, M, K, w_b, rank, x_q, s_x, t, tpg)
+#define DFSSM_QL(NV, NP)                                                                                         \
+    do {                                                                                                         \
+        if (K % 16 == 0)                                                                                         \
+            quantize_lora_down_kernel<NV, NP, true><<<grid, kQLThreads, lds, stream>>>(x, M, K, w_b, rank, x_q,  \
+                                                                                       s_x, t, tpg);             \
+        else                                                                                                     \
+            quantize_lora_down_kernel<NV, NP, false><<<grid, kQLThreads, lds, stream>>>(x, M, K, w_b, rank, x_q, \
+                                                                                        s_x, t, tpg);            \
+    } while (0)
     if (nv <= 4 && np <= 4) DFSSM_QL(4, 4);
     else if (nv <= 4) DFSSM_QL(4, 8);
     else if (nv <= 8 && np <= 4) DFSSM_QL(8, 4);
