@@ -12,12 +12,18 @@ Prints ONE JSON line.  `value` is whole-job HBM GB/s (algorithmic bytes of the
 step / time); `roofline` rates the dominant kernel (the GEMV launch, timed live
 with HIP events on its stream) against the 8 TB/s HBM peak; `cpu_baseline` is the
 plain C oracle on a bounded sample of the same workload on the host cores.
-Extra keys report the per-call hipGraph latency and the prefill (M=2048) int8
-MFMA throughput.
+Extra keys report the per-call hipGraph latency, the prefill (M=2048) int8 MFMA
+throughput, the in_proj decode shapes (M = 1, 4, 16 over 256 rotated copies), the
+literal 64-copy figure (warm: 74.5 MB sits in the Infinity Cache), the 48-layer
+decode sweep as hipGraph replays (warm, and cold over three rotated weight sets),
+and two probes from the same run: the back-to-back dispatch interval of an empty
+kernel and the device-to-device copy rate.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +38,16 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POPS)
 METRIC = "µs & HBM GB/s per scaffold+LoRA GEMV at M=1 (cold); int8 TOPS at M=2048"
 RANK = 16
+# HBM traffic of the GEMV launch from two rocprofv3 counter passes (FETCH_SIZE, then
+# WRITE_SIZE) over `bench.py --steps 5 --warmup 1 --no-extras --no-cpu-baseline
+# --copy-probe`, each counter scaled by what it reads for the 1 GiB copy in the same
+# run; written by `bench.py --traffic-from`.  Valid while the kernel's sources hash
+# to what was profiled.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "counters_gemv_kernel_out_proj_decode_512_copies.json")
+GEMV_SOURCES = ["bit_scaffold_int8_amd/csrc/gemv.hip", "bit_scaffold_int8_amd/csrc/device_common.h"]
+GEMV_KERNEL = "gemv_kernel<8, 1, 4, true>"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30
 
 
 def gemm_call_bytes(M, N, K):
@@ -52,6 +68,64 @@ def gemm_ops(M, N, K):
     return 2 * M * N * K + 2 * M * RANK * (K + N)
 
 
+def sources_sha256(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per GEMV launch from the committed counter summary; None if absent
+    or if the kernel's sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except OSError:
+        return None
+    if rec.get("sources_sha256") != sources_sha256(rec.get("sources", GEMV_SOURCES)):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def traffic_from(fetch_csv, write_csv, cmd):
+    """Turn two counter_collection.csv files into the traffic record and summary."""
+    def per_kernel(path, counter):
+        sums = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                for key in (GEMV_KERNEL, COPY_KERNEL):
+                    if key in r["Kernel_Name"]:
+                        sums.setdefault(key, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in sums.items()}, {k: len(v) for k, v in sums.items()}
+    fetch, nf = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, nw = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale = COPY_BYTES / 1024 / fetch[COPY_KERNEL]
+    w_scale = COPY_BYTES / 1024 / write[COPY_KERNEL]
+    read_b = fetch[GEMV_KERNEL] * f_scale * 1024
+    write_b = write[GEMV_KERNEL] * w_scale * 1024
+    alg = 512 * gemm_call_bytes(1, 2048, 4096)
+    rec = {
+        "kernel": GEMV_KERNEL, "workload": "out_proj decode M=1 K=4096 N=2048, 512 copies, one launch",
+        "command_fetch": cmd.replace("COUNTER", "FETCH_SIZE"), "command_write": cmd.replace("COUNTER", "WRITE_SIZE"),
+        "fetch_kib_per_launch": round(fetch[GEMV_KERNEL], 1), "write_kib_per_launch": round(write[GEMV_KERNEL], 1),
+        "launches": [nf[GEMV_KERNEL], nw[GEMV_KERNEL]],
+        "copy_fetch_kib": round(fetch[COPY_KERNEL], 1), "copy_write_kib": round(write[COPY_KERNEL], 1),
+        "copy_bytes_each_way": COPY_BYTES, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "hbm_read_bytes_per_launch": round(read_b), "hbm_write_bytes_per_launch": round(write_b),
+        "hbm_bytes_per_launch": round(read_b + write_b), "algorithmic_bytes_per_launch": alg,
+        "traffic_over_algorithmic": round((read_b + write_b) / alg, 4),
+        "sources": GEMV_SOURCES, "sources_sha256": sources_sha256(GEMV_SOURCES),
+    }
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -62,6 +136,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the per-call graph and prefill legs")
     ap.add_argument("--prefill-iters", type=int, default=10)
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the GEMV traffic record from two rocprofv3 counter_collection.csv files")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run the empty-kernel and copy probes even with --no-extras (counter calibration)")
     return ap.parse_args()
 
 
@@ -74,6 +152,108 @@ def time_events(torch, fn, iters, stream):
     e.record(stream)
     e.synchronize()
     return s.elapsed_time(e) / iters
+
+
+def decode_batched(torch, dp, stream, steps, warmup):
+    """(ms per whole step, ms per scaffold GEMV launch) of the strided-batched decode step."""
+    def step():
+        dp.quantize_lora_down(stream)
+        dp.gemm(stream, debug=False)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    step_ms = time_events(torch, step, steps, stream)
+    gemv_ms = time_events(torch, lambda: dp.gemm(stream, debug=False), steps, stream)
+    return step_ms, gemv_ms
+
+
+def probes(torch, stream):
+    """Empty-kernel dispatch interval and device copy rate, for context."""
+    for _ in range(20):
+        torch.cuda._sleep(0)
+    torch.cuda.synchronize()
+    empty_ms = time_events(torch, lambda: torch.cuda._sleep(0), 200, stream)
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    copy_ms = time_events(torch, lambda: b.copy_(a), 10, stream)
+    del a, b
+    return {"empty_kernel_us_back_to_back": round(empty_ms * 1e3, 2),
+            "copy_GBps_read_plus_write": round(2 * 4 * n / (copy_ms * 1e-3) / 1e9, 1),
+            "note": "torch.cuda._sleep(0) launches; a 1 GiB fp32 device-to-device copy_"}
+
+
+def in_proj_decode(torch, dev, stream, steps, warmup):
+    """in_proj decode (K=2048, N=8512) at M = 1, 4, 16 over 256 rotated copies (619 MB
+    of weights, cold).  One weight stream is drawn with 16-token inputs; M = 1 and 4
+    use the first M rows of each copy's input."""
+    import synth_inputs as si
+    from bit_scaffold_int8_amd.runner import DeviceProjections
+    R, (_, N, K, n_out) = 256, si.CONFIGS["in_proj_decode_k2048_n8512"]["shapes"][2]
+    base = DeviceProjections.from_problems(
+        si.make_copies(16, N, K, n_out, seed=si.CONFIGS["in_proj_decode_k2048_n8512"]["seed"], copies=R), device=dev)
+    out = {"copies_rotated": R, "K": K, "N": N}
+    for M in (1, 4, 16):
+        dp = DeviceProjections(
+            x=base.x[:, :M].contiguous(), w_bits=base.w_bits, s_w=base.s_w, w_a=base.w_a, s_a=base.s_a,
+            w_b=base.w_b, s_b=base.s_b,
+            x_q=torch.empty((R, M, K), dtype=torch.int8, device=dev),
+            s_x=torch.empty((R, M), dtype=torch.float32, device=dev),
+            t=torch.empty((R, M, 16), dtype=torch.int32, device=dev),
+            y=torch.empty((R, M, N), dtype=torch.float32, device=dev), acc_dbg=None)
+        step_ms, gemv_ms = decode_batched(torch, dp, stream, steps, warmup)
+        out[f"M{M}"] = {"us_per_step_per_copy": round(step_ms * 1e3 / R, 4),
+                        "step_GBps": round(R * step_bytes(M, N, K) / (step_ms * 1e-3) / 1e9, 1),
+                        "gemv_launch_us": round(gemv_ms * 1e3, 2),
+                        "gemv_GBps": round(R * gemm_call_bytes(M, N, K) / (gemv_ms * 1e-3) / 1e9, 1)}
+        del dp
+    del base
+    return out
+
+
+def decode_sweep_48l(torch, dev, replays):
+    """48 layers x (in_proj, out_proj) at M = 1, one token = 96 single-problem calls
+    (2 launches each) captured in one hipGraph.  Warm: one weight set (172 MB, fits
+    the Infinity Cache) replayed back to back.  Cold: three weight sets drawn from the
+    same stream, replayed in rotation (515 MB)."""
+    import synth_inputs as si
+    from bit_scaffold_int8_amd.runner import DeviceProjections
+    cfg = si.CONFIGS["decode_sweep_48l"]
+    rng = np.random.default_rng(cfg["seed"])
+    sets = []
+    for _ in range(3):
+        sets.append([DeviceProjections.from_problems([si.draw_problem(rng, M, N, K, o)], device=dev)
+                     for _layer in range(cfg["layers"]) for (M, N, K, o) in cfg["shapes"]])
+    token_bytes = cfg["layers"] * sum(step_bytes(M, N, K) for (M, N, K, _) in cfg["shapes"])
+    cs = torch.cuda.Stream()
+    graphs = []
+    for projs in sets:
+        with torch.cuda.stream(cs):
+            for p in projs:
+                p.forward(cs, debug=False)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cs):
+            for p in projs:
+                p.forward(torch.cuda.current_stream(), debug=False)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        graphs.append(g)
+    cur = torch.cuda.current_stream()
+    warm_ms = time_events(torch, graphs[0].replay, replays, cur)
+    it = iter(range(10 ** 9))
+    cold_ms = time_events(torch, lambda: graphs[next(it) % 3].replay(), 3 * replays, cur)
+    del graphs, sets
+    return {"layers": cfg["layers"], "launches_per_token": 4 * cfg["layers"],
+            "bytes_per_token": token_bytes,
+            "warm_us_per_token": round(warm_ms * 1e3, 1),
+            "warm_GBps": round(token_bytes / (warm_ms * 1e-3) / 1e9, 1),
+            "cold_us_per_token": round(cold_ms * 1e3, 1),
+            "cold_GBps": round(token_bytes / (cold_ms * 1e-3) / 1e9, 1),
+            "note": "one hipGraph per token of 96 single-problem calls; cold rotates 3 weight sets"}
 
 
 def cpu_baseline(probs, seconds):
@@ -97,6 +277,11 @@ def cpu_baseline(probs, seconds):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from,
+                     "rocprofv3 --pmc COUNTER -d gpurun_out/pmc_COUNTER -o run --output-format csv -- python -u bench.py "
+                     "--steps 5 --warmup 1 --no-extras --no-cpu-baseline --copy-probe")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the projection is not sharded "
               "across GPUs in this build.", file=sys.stderr)
@@ -172,7 +357,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "avg_launch_us": round(gemv_ms * 1e3, 3),
             "timing": "HIP events around back-to-back launches on the kernel's stream",
             "algorithmic_bytes_per_launch": R * gemm_call_bytes(M, N, K),
@@ -221,6 +406,25 @@ def main():
                          "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
             del pp
         out["prefill_m2048"] = pre
+
+        # the literal 64-copy figure (74.5 MB: warm in the Infinity Cache)
+        dp64 = DeviceProjections(
+            x=dp.x[:64], w_bits=dp.w_bits[:64], s_w=dp.s_w[:64], w_a=dp.w_a[:64], s_a=dp.s_a[:64],
+            w_b=dp.w_b[:64], s_b=dp.s_b[:64], x_q=dp.x_q[:64], s_x=dp.s_x[:64], t=dp.t[:64], y=dp.y[:64],
+            acc_dbg=None)
+        s64, g64 = decode_batched(torch, dp64, stream, args.steps, args.warmup)
+        out["out_proj_decode_64_copies"] = {
+            "step_GBps": round(64 * step_bytes(M, N, K) / (s64 * 1e-3) / 1e9, 1),
+            "us_per_step_per_copy": round(s64 * 1e3 / 64, 4),
+            "gemv_launch_us": round(g64 * 1e3, 2),
+            "gemv_GBps": round(64 * gemm_call_bytes(M, N, K) / (g64 * 1e-3) / 1e9, 1),
+            "note": "warm: 64 copies fit the 256 MB Infinity Cache"}
+        out["in_proj_decode_k2048_n8512"] = in_proj_decode(torch, dev, stream, args.steps, args.warmup)
+        out["decode_sweep_48l"] = decode_sweep_48l(torch, dev, 10)
+        out["probes"] = probes(torch, stream)
+
+    if args.no_extras and args.copy_probe:
+        out["probes"] = probes(torch, stream)
 
     if not args.no_cpu_baseline:
         res = cpu_baseline(probs, args.cpu_seconds)
