@@ -4,14 +4,16 @@ Default workload: the Mamba-2 1.3B-shaped out_proj decode step (M=1 token, K=409
 N=2048, rank-16 int8 LoRA), cold cache: `--copies` independent weight sets
 (512 x 1.16 MB = 596 MB, above the 256 MB Infinity Cache) are rotated so every
 step streams its packed weights from HBM.  One step = the whole hot path over all
-copies: per-token absmax int8 quantization + LoRA down (one launch for all copies),
-then the bit-unpack scaffold GEMV with the fused scale/LoRA-up epilogue (one
-launch for all copies).  Inputs are resident in HBM before the timed region.
+copies in one launch (dfssm_scaffold_lora_forward_strided_batched): per-token absmax
+int8 quantization, the LoRA down-projection, the bit-unpack scaffold GEMV and the
+fused scale/LoRA-up epilogue.  Inputs are resident in HBM before the timed region.
 
 Prints ONE JSON line.  `value` is whole-job HBM GB/s (algorithmic bytes of the
-step / time); `roofline` rates the dominant kernel (the GEMV launch, timed live
-with HIP events on its stream) against the 8 TB/s HBM peak; `cpu_baseline` is the
-plain C oracle on a bounded sample of the same workload on the host cores.
+step / time); `roofline` rates the dominant kernel (the step's one launch, timed
+live with HIP events on its stream) against the 8 TB/s HBM peak; `cpu_baseline` is
+the plain C oracle on a bounded sample of the same workload on the host cores.
+`two_call_step` times the same step as the two-call form (quantize + LoRA-down
+launch, then the scaffold GEMV launch).
 Extra keys report the per-call hipGraph latency, the prefill (M=2048) int8 MFMA
 throughput, the in_proj decode shapes (M = 1, 4, 16 over 256 rotated copies), the
 literal 64-copy figure (warm: 74.5 MB sits in the Infinity Cache), the 48-layer
@@ -45,7 +47,7 @@ RANK = 16
 # to what was profiled.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "counters_gemv_kernel_out_proj_decode_512_copies.json")
 GEMV_SOURCES = ["bit_scaffold_int8_amd/csrc/gemv.hip", "bit_scaffold_int8_amd/csrc/device_common.h"]
-GEMV_KERNEL = "gemv_kernel<8, 1, 4, true>"
+GEMV_KERNEL = "gemv_kernel<8, 1, 4, true, true>"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30
 
@@ -107,7 +109,7 @@ def traffic_from(fetch_csv, write_csv, cmd):
     w_scale = COPY_BYTES / 1024 / write[COPY_KERNEL]
     read_b = fetch[GEMV_KERNEL] * f_scale * 1024
     write_b = write[GEMV_KERNEL] * w_scale * 1024
-    alg = 512 * gemm_call_bytes(1, 2048, 4096)
+    alg = 512 * step_bytes(1, 2048, 4096)
     rec = {
         "kernel": GEMV_KERNEL, "workload": "out_proj decode M=1 K=4096 N=2048, 512 copies, one launch",
         "command_fetch": cmd.replace("COUNTER", "FETCH_SIZE"), "command_write": cmd.replace("COUNTER", "WRITE_SIZE"),
@@ -130,7 +132,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--copies", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -155,16 +157,22 @@ def time_events(torch, fn, iters, stream):
 
 
 def decode_batched(torch, dp, stream, steps, warmup):
-    """(ms per whole step, ms per scaffold GEMV launch) of the strided-batched decode step."""
-    def step():
+    """(ms per one-call step, ms per two-call step, ms per scaffold GEMV launch of the
+    two-call form) of the strided-batched decode step."""
+    def one():
+        dp.forward_one_call(stream, debug=False)
+
+    def two():
         dp.quantize_lora_down(stream)
         dp.gemm(stream, debug=False)
     for _ in range(warmup):
-        step()
+        one()
+        two()
     torch.cuda.synchronize()
-    step_ms = time_events(torch, step, steps, stream)
+    one_ms = time_events(torch, one, steps, stream)
+    two_ms = time_events(torch, two, steps, stream)
     gemv_ms = time_events(torch, lambda: dp.gemm(stream, debug=False), steps, stream)
-    return step_ms, gemv_ms
+    return one_ms, two_ms, gemv_ms
 
 
 def probes(torch, stream):
@@ -203,9 +211,10 @@ def in_proj_decode(torch, dev, stream, steps, warmup):
             s_x=torch.empty((R, M), dtype=torch.float32, device=dev),
             t=torch.empty((R, M, 16), dtype=torch.int32, device=dev),
             y=torch.empty((R, M, N), dtype=torch.float32, device=dev), acc_dbg=None)
-        step_ms, gemv_ms = decode_batched(torch, dp, stream, steps, warmup)
+        step_ms, two_ms, gemv_ms = decode_batched(torch, dp, stream, steps, warmup)
         out[f"M{M}"] = {"us_per_step_per_copy": round(step_ms * 1e3 / R, 4),
                         "step_GBps": round(R * step_bytes(M, N, K) / (step_ms * 1e-3) / 1e9, 1),
+                        "two_call_step_GBps": round(R * step_bytes(M, N, K) / (two_ms * 1e-3) / 1e9, 1),
                         "gemv_launch_us": round(gemv_ms * 1e3, 2),
                         "gemv_GBps": round(R * gemm_call_bytes(M, N, K) / (gemv_ms * 1e-3) / 1e9, 1)}
         del dp
@@ -232,12 +241,12 @@ def decode_sweep_48l(torch, dev, replays):
     for projs in sets:
         with torch.cuda.stream(cs):
             for p in projs:
-                p.forward(cs, debug=False)
+                p.forward_one_call(cs, debug=False)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cs):
             for p in projs:
-                p.forward(torch.cuda.current_stream(), debug=False)
+                p.forward_one_call(torch.cuda.current_stream(), debug=False)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -247,13 +256,13 @@ def decode_sweep_48l(torch, dev, replays):
     it = iter(range(10 ** 9))
     cold_ms = time_events(torch, lambda: graphs[next(it) % 3].replay(), 3 * replays, cur)
     del graphs, sets
-    return {"layers": cfg["layers"], "launches_per_token": 4 * cfg["layers"],
+    return {"layers": cfg["layers"], "launches_per_token": 2 * cfg["layers"],
             "bytes_per_token": token_bytes,
             "warm_us_per_token": round(warm_ms * 1e3, 1),
             "warm_GBps": round(token_bytes / (warm_ms * 1e-3) / 1e9, 1),
             "cold_us_per_token": round(cold_ms * 1e3, 1),
             "cold_GBps": round(token_bytes / (cold_ms * 1e-3) / 1e9, 1),
-            "note": "one hipGraph per token of 96 single-problem calls; cold rotates 3 weight sets"}
+            "note": "one hipGraph per token of 96 single-problem one-call projections; cold rotates 3 weight sets"}
 
 
 def cpu_baseline(probs, seconds):
@@ -305,8 +314,7 @@ def main():
     weight_bytes = R * (N * K // 8 + 4 * N + 16 * N + 4 * N + 16 * K + 4 * RANK)
 
     def step():
-        dp.quantize_lora_down(stream)
-        dp.gemm(stream, debug=False)
+        dp.forward_one_call(stream, debug=False)
 
     for _ in range(args.warmup):
         step()
@@ -323,13 +331,17 @@ def main():
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
 
-    # the dominant kernel (the scaffold GEMV launch over all copies), timed live on its
+    # the dominant kernel (the step's one launch over all copies), timed live on its
     # stream: K back-to-back launches between two events, so the average is the
     # kernel's duration plus only the dispatch gap between consecutive launches
+    launch_ms = time_events(torch, step, args.steps, stream)
+    # the same step as two calls (quantize + LoRA-down, then the scaffold GEMV)
+    two_ms = time_events(torch, lambda: (dp.quantize_lora_down(stream), dp.gemm(stream, debug=False)),
+                         args.steps, stream)
     gemv_ms = time_events(torch, lambda: dp.gemm(stream, debug=False), args.steps, stream)
 
     value = R * step_bytes(M, N, K) / (ms_per_step * 1e-3) / 1e9
-    achieved = R * gemm_call_bytes(M, N, K) / (gemv_ms * 1e-3) / 1e9
+    achieved = R * step_bytes(M, N, K) / (launch_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -347,20 +359,26 @@ def main():
             "workload": "out_proj_decode_m1_k4096_n2048",
             "M": M, "K": K, "N": N, "rank": RANK,
             "copies_rotated": R, "rotated_weight_bytes": weight_bytes,
-            "launch": "strided-batched: 2 launches per step (quantize+LoRA-down, scaffold GEMV) over all copies",
+            "launch": "one strided-batched launch per step over all copies (dfssm_scaffold_lora_forward)",
         },
         "us_per_gemv_step": round(ms_per_step * 1e3 / R, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_kernel (dfssm_scaffold_lora_gemm_strided_batched, M=1)",
+            "kernel": "gemv_kernel, fused variant (dfssm_scaffold_lora_forward_strided_batched, M=1)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(),
-            "avg_launch_us": round(gemv_ms * 1e3, 3),
+            "avg_launch_us": round(launch_ms * 1e3, 3),
             "timing": "HIP events around back-to-back launches on the kernel's stream",
-            "algorithmic_bytes_per_launch": R * gemm_call_bytes(M, N, K),
+            "algorithmic_bytes_per_launch": R * step_bytes(M, N, K),
+        },
+        "two_call_step": {
+            "us_per_step": round(two_ms * 1e3, 2),
+            "GBps": round(R * step_bytes(M, N, K) / (two_ms * 1e-3) / 1e9, 1),
+            "gemv_launch_us": round(gemv_ms * 1e3, 2),
+            "gemv_GBps": round(R * gemm_call_bytes(M, N, K) / (gemv_ms * 1e-3) / 1e9, 1),
         },
     }
 
@@ -370,27 +388,29 @@ def main():
             x=dp.x[b:b + 1], w_bits=dp.w_bits[b:b + 1], s_w=dp.s_w[b:b + 1], w_a=dp.w_a[b:b + 1],
             s_a=dp.s_a[b:b + 1], w_b=dp.w_b[b:b + 1], s_b=dp.s_b[b:b + 1], x_q=dp.x_q[b:b + 1],
             s_x=dp.s_x[b:b + 1], t=dp.t[b:b + 1], y=dp.y[b:b + 1], acc_dbg=None) for b in range(R)]
-        g = torch.cuda.CUDAGraph()
         cs = torch.cuda.Stream()
-        with torch.cuda.stream(cs):
-            for p in single[:4]:
-                p.forward(cs, debug=False)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=cs):
-            for p in single:
-                p.forward(torch.cuda.current_stream(), debug=False)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        reps = 5
-        graph_ms = time_events(torch, g.replay, reps, torch.cuda.current_stream())
-        us_call = graph_ms * 1e3 / R
-        out["per_call_graph"] = {
-            "us_per_call": round(us_call, 3),
-            "GBps": round(step_bytes(M, N, K) / (us_call * 1e-6) / 1e9, 2),
-            "launches_per_call": 2,
-            "note": "R rotated single-problem calls (2 kernels each) captured in one hipGraph",
-        }
+        per_call = {}
+        for name, fwd in (("one_call", lambda p, s: p.forward_one_call(s, debug=False)),
+                          ("two_call", lambda p, s: p.forward(s, debug=False))):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cs):
+                for p in single[:4]:
+                    fwd(p, cs)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cs):
+                for p in single:
+                    fwd(p, torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            graph_ms = time_events(torch, g.replay, 5, torch.cuda.current_stream())
+            us_call = graph_ms * 1e3 / R
+            per_call[name] = {"us_per_call": round(us_call, 3),
+                              "GBps": round(step_bytes(M, N, K) / (us_call * 1e-6) / 1e9, 2),
+                              "launches_per_call": 1 if name == "one_call" else 2}
+            del g
+        per_call["note"] = "R rotated single-problem calls captured in one hipGraph"
+        out["per_call_graph"] = per_call
 
         # prefill: M=2048 tokens on the int8 MFMA path
         pre = {}
@@ -412,10 +432,11 @@ def main():
             x=dp.x[:64], w_bits=dp.w_bits[:64], s_w=dp.s_w[:64], w_a=dp.w_a[:64], s_a=dp.s_a[:64],
             w_b=dp.w_b[:64], s_b=dp.s_b[:64], x_q=dp.x_q[:64], s_x=dp.s_x[:64], t=dp.t[:64], y=dp.y[:64],
             acc_dbg=None)
-        s64, g64 = decode_batched(torch, dp64, stream, args.steps, args.warmup)
+        s64, t64, g64 = decode_batched(torch, dp64, stream, args.steps, args.warmup)
         out["out_proj_decode_64_copies"] = {
             "step_GBps": round(64 * step_bytes(M, N, K) / (s64 * 1e-3) / 1e9, 1),
             "us_per_step_per_copy": round(s64 * 1e3 / 64, 4),
+            "two_call_step_GBps": round(64 * step_bytes(M, N, K) / (t64 * 1e-3) / 1e9, 1),
             "gemv_launch_us": round(g64 * 1e3, 2),
             "gemv_GBps": round(64 * gemm_call_bytes(M, N, K) / (g64 * 1e-3) / 1e9, 1),
             "note": "warm: 64 copies fit the 256 MB Infinity Cache"}

@@ -23,6 +23,11 @@ hipError_t launch_gemm_mfma(const int8_t* x_q, const float* s_x, int64_t M, int6
                             const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
                             const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
                             int64_t batch, hipStream_t stream);
+bool decode_fused_supported(int64_t M, int64_t K);
+hipError_t launch_decode_fused(const float* x, int M, int64_t N, int64_t K, const uint8_t* w_bits,
+                               const float* s_w, const int8_t* w_a, const float* s_a, const int8_t* w_b,
+                               const float* s_b, int rank, int8_t* x_q, float* s_x, int32_t* t, float* y,
+                               int32_t* acc_dbg, int64_t batch, hipStream_t stream);
 bool prefill_supported(int64_t M, int64_t N, int64_t K);
 int prefill_num_cfgs();
 hipError_t launch_gemm_prefill(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
@@ -132,6 +137,36 @@ dfssm_status gemm_impl(const int8_t* x_q, const float* s_x, int64_t M, int64_t N
     return e == hipSuccess ? DFSSM_OK : DFSSM_ERR_HIP;
 }
 
+dfssm_status forward_impl(const float* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_bits,
+                          const float* s_w, const int8_t* w_a, const float* s_a, const int8_t* w_b,
+                          const float* s_b, int32_t rank, int8_t* x_q, float* s_x, int32_t* t, float* y,
+                          int32_t* acc_dbg, int64_t batch, hipStream_t stream) {
+    // the two calls' checks, in full, before anything is launched
+    if (!x || !x_q || !s_x || !w_bits || !s_w || !y) return DFSSM_ERR_INVALID_ARG;
+    if (dfssm_status st = check_sizes(M, K, batch)) return st;
+    if (N <= 0 || N >= kMaxRows || (K % 8) != 0) return DFSSM_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(x_q) || !aligned4(s_x) || !aligned16(w_bits) || !aligned4(s_w) ||
+        !aligned4(y) || !aligned4_or_null(acc_dbg))
+        return DFSSM_ERR_INVALID_ARG;
+    if (dfssm_status st = check_rank(rank)) return st;
+    if (rank == 16) {
+        if (!w_a || !s_a || !w_b || !s_b || !t) return DFSSM_ERR_INVALID_ARG;
+        if (!aligned16(w_a) || !aligned4(s_a) || !aligned16(w_b) || !aligned4(s_b) || !aligned4(t))
+            return DFSSM_ERR_INVALID_ARG;
+    }
+    if (K > kMaxK) return DFSSM_ERR_UNSUPPORTED;
+    if (M * batch >= kMaxRows) return DFSSM_ERR_INVALID_ARG;
+    const bool gemv_fits = N * (K / 8) < ((int64_t)1 << 31) && M * N * 4 < ((int64_t)1 << 31);
+    if (gemv_fits && dfssm::decode_fused_supported(M, K)) {
+        const hipError_t e = dfssm::launch_decode_fused(x, (int)M, N, K, w_bits, s_w, w_a, s_a, w_b, s_b, rank, x_q,
+                                                        s_x, t, y, acc_dbg, batch, stream);
+        if (e != hipErrorNotSupported) return e == hipSuccess ? DFSSM_OK : DFSSM_ERR_HIP;
+        // the launch plan has several groups per problem at a throughput batch: two kernels
+    }
+    if (dfssm_status st = quantize_lora_down_impl(x, M, K, w_b, rank, x_q, s_x, t, batch, stream)) return st;
+    return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -146,7 +181,7 @@ const char* dfssm_status_string(dfssm_status status) {
     return "DFSSM_ERR_UNKNOWN";
 }
 
-int32_t dfssm_version(void) { return 200; }
+int32_t dfssm_version(void) { return 300; }
 
 dfssm_status dfssm_quantize_act(const float* x, int64_t M, int64_t K, int8_t* x_q, float* s_x,
                                 hipStream_t stream) {
@@ -190,6 +225,22 @@ dfssm_status dfssm_scaffold_lora_gemm_strided_batched(const int8_t* x_q, const f
                                                       const int32_t* t, int32_t rank, float* y, int32_t* acc_dbg,
                                                       int64_t batch, hipStream_t stream) {
     return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, stream);
+}
+
+dfssm_status dfssm_scaffold_lora_forward(const float* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_bits,
+                                         const float* s_w, const int8_t* w_a, const float* s_a, const int8_t* w_b,
+                                         const float* s_b, int32_t rank, int8_t* x_q, float* s_x, int32_t* t,
+                                         float* y, int32_t* acc_dbg, hipStream_t stream) {
+    return forward_impl(x, M, N, K, w_bits, s_w, w_a, s_a, w_b, s_b, rank, x_q, s_x, t, y, acc_dbg, 1, stream);
+}
+
+dfssm_status dfssm_scaffold_lora_forward_strided_batched(const float* x, int64_t M, int64_t N, int64_t K,
+                                                         const uint8_t* w_bits, const float* s_w, const int8_t* w_a,
+                                                         const float* s_a, const int8_t* w_b, const float* s_b,
+                                                         int32_t rank, int8_t* x_q, float* s_x, int32_t* t,
+                                                         float* y, int32_t* acc_dbg, int64_t batch,
+                                                         hipStream_t stream) {
+    return forward_impl(x, M, N, K, w_bits, s_w, w_a, s_a, w_b, s_b, rank, x_q, s_x, t, y, acc_dbg, batch, stream);
 }
 
 }  // extern "C"

@@ -28,8 +28,20 @@
 //    waited for early), and the barriers between stages order LDS only, so the
 //    prefetched loads stay in flight across them.
 #include "device_common.h"
+#include "quant_common.h"
 
 namespace dfssm {
+
+// Operands of the fused variant, which also quantizes the tokens and computes the LoRA
+// down-projection t = W_B x_q itself (one launch per projection).  Outputs x_q, s_x and
+// t are written by the first group of each problem; every group computes them alike.
+struct FusedIO {
+    const float* x;     // fp32 [M][K]
+    const int8_t* w_b;  // int8 [16][K] (rank 16) or unused
+    int8_t* x_q;        // int8 [M][K]  (out)
+    float* s_x;         // fp32 [M]     (out)
+    int32_t* t;         // int32 [M][16] (out, rank 16)
+};
 
 // Rows one workgroup owns at most (their epilogue operands live in LDS): 2048 for the
 // 8-wave, 4-tile-stage shape that large batches run (one group per 2048-row problem),
@@ -38,13 +50,16 @@ constexpr int gemv_rows_cap(int W, int T) { return (W >= 8 && T >= 4) ? 2048 : 1
 
 // One lane group = 16 lanes; one chunk = 16 packed bytes = 128 k of one row.
 // W waves split K; C chunks per lane; T row tiles (16 rows each) per stage.
-template <int W, int C, int T, bool kFast>
+// kFused: quantize x and compute t in the setup (x_q, s_x, t are then outputs; needs
+// the 16-byte path, one chunk per lane, M <= 4 and M K <= 1024 W).
+template <int W, int C, int T, bool kFast, bool kFused>
 __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     const int8_t* __restrict__ x_q, const float* __restrict__ s_x, int M, int64_t N, int64_t K,
     const uint8_t* __restrict__ w_bits, const float* __restrict__ s_w,
     const int8_t* __restrict__ w_a, const float* __restrict__ s_a, const float* __restrict__ s_b,
     const int32_t* __restrict__ t, int rank, float* __restrict__ y, int32_t* __restrict__ acc_dbg,
-    int64_t num_tiles, int stages_per_wg) {
+    int64_t num_tiles, int stages_per_wg, FusedIO fio) {
+    static_assert(!kFused || (kFast && C == 1), "the fused setup needs whole 128-k chunks, one per lane");
     // epilogue: thread -> one row of the stage (its W_A row, s_A, s_w are loaded once per
     // stage) and E of that row's tokens
     static_assert((W * kWave) % (T * 16) == 0, "a stage's rows must divide the group size");
@@ -64,6 +79,11 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     __shared__ int32_t xsum[16];
     __shared__ float u[16][kRank];
     __shared__ float sxs[16];
+    // fused setup only: the tokens' codes, per-wave absmax partials, the t tile
+    constexpr int kFusedMK = 1024 * W;  // largest M K the fused setup takes
+    __shared__ __align__(16) uint32_t codes_lds[kFused ? kFusedMK / 4 : 1];
+    __shared__ float amax_part[kFused ? W : 1][4];
+    __shared__ int32_t tsum[kFused ? 16 : 1][kRank];
 
     // problem blockIdx.y of a dense batch (every operand advanced by its own size)
     {
@@ -157,79 +177,241 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
         }
     }
 
-    // token scales and the LoRA down-projection: loaded now, stored to LDS after the
-    // activation loads below have been issued too
     constexpr int U = (16 * kRank + W * kWave - 1) / (W * kWave);
-    float tv[U], sbv[U];
-#pragma unroll
-    for (int q = 0; q < U; ++q) {
-        const int e = threadIdx.x + q * W * kWave;
-        const int tok = e / kRank, r = e % kRank;
-        const bool live = e < 16 * kRank && tok < M;
-        if (rank != 0) {
-            const uint32_t m = opaque_mask(live);
-            tv[q] = (float)(int32_t)((uint32_t)t[(live ? tok : 0) * kRank + r] & m);
-            sbv[q] = __uint_as_float(__float_as_uint(s_b[r]) & m);
-        } else {
-            tv[q] = 0.0f;
-            sbv[q] = 0.0f;
-        }
-    }
-    const float sxv = __uint_as_float(__float_as_uint(s_x[threadIdx.x < M ? threadIdx.x : 0]) &
-                                      opaque_mask(threadIdx.x < M));
-
-    // Activations of token i in bit-plane order, for this lane's chunks.
     v4i X[C][8];
-    int32_t xpart = 0;
-    const uint8_t* xrow = reinterpret_cast<const uint8_t*>(x_q) + (i < M ? (int64_t)i * K : 0);
-    const int64_t xlimit = i < M ? K : 0;
+    if constexpr (kFused) {
+        // ---- fused setup: quantize the tokens (every group alike), build the
+        // plane-ordered activations from the codes, and t = W_B x_q as one more 16-row
+        // MFMA tile whose rows are W_B's ranks.
+        constexpr int NT = W * kWave;
+        constexpr int kXV = kFusedMK / 4 / NT;  // float4 of the rows per thread (4)
+        const int64_t p = blockIdx.y;
+        const bool writer = blockIdx.x == 0;
+        const int64_t MK4 = (int64_t)M * K / 4;
+        for (int e = threadIdx.x; e < 16 * kRank; e += NT) (&tsum[0][0])[e] = 0;
+        for (int e = threadIdx.x; e < 2 * T * 16 * 20; e += NT) (&red[0][0][0])[e] = 0;
+
+        // loads: the rows (float4 f = e NT + tid of the dense [M][K] block), this lane's
+        // 128-k chunk of W_B row i as eight 16-byte pieces, and s_B
+        const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(fio.x + p * M * K, (uint32_t)(M * K * 4));
+        float4 xv[kXV];
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-        const int64_t q = ((int64_t)c * W + wave) * 4 + g;
-        const int64_t kb = 128 * q;
-        uint32_t nat[32];
+        for (int e = 0; e < kXV; ++e) {
+            const v4f v = __builtin_bit_cast(
+                v4f, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (e * NT + (int)threadIdx.x) * 16, 0, 0));
+            xv[e] = make_float4(v[0], v[1], v[2], v[3]);
+        }
+        const int qch = wave * 4 + g;            // this lane's chunk (C == 1)
+        const bool chunk_live = 128 * qch < K;   // K % 128 == 0: whole chunks only
+        const __amdgpu_buffer_rsrc_t wb_rsrc =
+            make_rsrc(rank != 0 ? fio.w_b + p * kRank * K : fio.w_b, rank != 0 ? (uint32_t)(kRank * K) : 0u);
+        v4i wbv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint4 v = kFast ? load16_select(xrow, kb + 16 * e, kb + 16 * e < xlimit)
-                                  : load16_guarded<false>(xrow, kb + 16 * e, xlimit);
-            nat[4 * e + 0] = v.x;
-            nat[4 * e + 1] = v.y;
-            nat[4 * e + 2] = v.z;
-            nat[4 * e + 3] = v.w;
+        for (int e = 0; e < 8; ++e)
+            wbv[e] = __builtin_amdgcn_raw_buffer_load_b128(
+                wb_rsrc, chunk_live ? (int)(i * K + 128 * qch + 16 * e) : kOffDead - 64, 0, 0);
+        float sbv[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+            const int e = threadIdx.x + q * NT;
+            sbv[q] = rank != 0 ? s_b[e % kRank] : 0.0f;
+        }
+
+        // per-token absmax: per thread, per wave, then across waves through LDS
+        auto token_of = [&](int e) {
+            const int64_t f = (int64_t)e * NT + threadIdx.x;
+            const int64_t m = f * 4 / K;
+            return (int)(m < 3 ? m : 3);  // past the rows: zero values, any token
+        };
+        float am[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int e = 0; e < kXV; ++e) {
+            const int m = token_of(e);
+            const float a = absmax4(xv[e]);
+#pragma unroll
+            for (int mm = 0; mm < 4; ++mm)
+                if (m == mm) am[mm] = fmaxf(am[mm], a);
         }
 #pragma unroll
-        for (int e = 0; e < 32; ++e) xpart = byte_sum(nat[e], xpart);
+        for (int mm = 0; mm < 4; ++mm) {
+            if (mm < M) {
+                const float w = wave_max(am[mm]);
+                if (lane == 0) amax_part[wave][mm] = w;
+            }
+        }
+        lds_barrier();
+        float sc[4], inv[4], amx[4];
+        bool fast[4];
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+            float a = 0.0f;
+            if (mm < M)
+                for (int w = 0; w < W; ++w) a = fmaxf(a, amax_part[w][mm]);
+            const RowScale rs = row_scale(a);
+            amx[mm] = a;
+            sc[mm] = a == 0.0f ? 0.0f : rs.s;
+            inv[mm] = rs.inv;
+            fast[mm] = rs.fast;
+        }
+
+        // codes into LDS (and x_q, s_x from the problem's first group)
+        const __amdgpu_buffer_rsrc_t xq_rsrc = make_rsrc(fio.x_q + p * M * K, writer ? (uint32_t)(M * K) : 0u);
+#pragma unroll
+        for (int e = 0; e < kXV; ++e) {
+            const int f = e * NT + (int)threadIdx.x;
+            const int m = token_of(e);
+            float a = amx[0], s = sc[0], iv = inv[0];
+            bool fs = fast[0];
+#pragma unroll
+            for (int mm = 1; mm < 4; ++mm)
+                if (m == mm) { a = amx[mm]; s = sc[mm]; iv = inv[mm]; fs = fast[mm]; }
+            uint32_t n4 = 0;
+            uint32_t q = a == 0.0f ? 0u : fast_code4(xv[e], iv, n4);
+            // rare: a code within reach of a rounding tie is redone with the IEEE quotient
+            if (a != 0.0f && (!fs || n4)) q = exact_code4(xv[e], s);
+            if (f < MK4) codes_lds[f] = q;
+            __builtin_amdgcn_raw_buffer_store_b32(q, xq_rsrc, f < MK4 ? 4 * f : kOffDead, 0, 0);
+        }
+        if (threadIdx.x < 16) {
+            float s = 0.0f;
+#pragma unroll
+            for (int mm = 0; mm < 4; ++mm)
+                if ((int)threadIdx.x == mm && mm < M) s = sc[mm];
+            sxs[threadIdx.x] = s;
+            if (writer && (int)threadIdx.x < M) fio.s_x[p * M + threadIdx.x] = s;
+        }
+        lds_barrier();
+
+        // this lane's chunk of token i's codes, two 16-byte pieces at a time: the t
+        // MFMAs take them in natural order, the scaffold operand in bit-plane order
+        const uint8_t* crow = reinterpret_cast<const uint8_t*>(codes_lds) + (i < M ? i * K : 0);
+        const bool xlive = i < M && chunk_live;
+        int32_t xpart = 0;
+        v4i acc_t = {0, 0, 0, 0};
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
+            uint32_t nat[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int e = 2 * qq + h;
+                const uint4 v = xlive ? *reinterpret_cast<const uint4*>(crow + 128 * qch + 16 * e)
+                                      : make_uint4(0u, 0u, 0u, 0u);
+                nat[4 * h + 0] = v.x;
+                nat[4 * h + 1] = v.y;
+                nat[4 * h + 2] = v.z;
+                nat[4 * h + 3] = v.w;
+                const v4i bv = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+                acc_t = __builtin_amdgcn_mfma_i32_16x16x64_i8(wbv[e], bv, acc_t, 0, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xpart = byte_sum(nat[e], xpart);
 #pragma unroll
             for (int jh = 0; jh < 2; ++jh) {
                 uint32_t o0, o1, o2, o3;
-                transpose4x4(nat[8 * qq + 0 + jh], nat[8 * qq + 2 + jh], nat[8 * qq + 4 + jh],
-                             nat[8 * qq + 6 + jh], o0, o1, o2, o3);
-                X[c][4 * jh + 0][qq] = (int)o0;
-                X[c][4 * jh + 1][qq] = (int)o1;
-                X[c][4 * jh + 2][qq] = (int)o2;
-                X[c][4 * jh + 3][qq] = (int)o3;
+                transpose4x4(nat[0 + jh], nat[2 + jh], nat[4 + jh], nat[6 + jh], o0, o1, o2, o3);
+                X[0][4 * jh + 0][qq] = (int)o0;
+                X[0][4 * jh + 1][qq] = (int)o1;
+                X[0][4 * jh + 2][qq] = (int)o2;
+                X[0][4 * jh + 3][qq] = (int)o3;
             }
         }
-    }
-    // LoRA: u[tok][r] = s_B[r] * t[tok][r] (fp32), shared by every output row.
+        // D[4g + v][i] = t[token i][rank 4g + v]: the waves' partial sums meet in LDS
+        if (i < M) {
 #pragma unroll
-    for (int q = 0; q < U; ++q) {
-        const int e = threadIdx.x + q * W * kWave;
-        if (e < 16 * kRank) u[e / kRank][e % kRank] = sbv[q] * tv[q];
+            for (int v = 0; v < 4; ++v) atomicAdd(&tsum[i][4 * g + v], acc_t[v]);
+        }
+        xs_part[wave][lane] = xpart;
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+            const int e = threadIdx.x + q * NT;
+            if (e < 16 * kRank) {
+                const int tok = e / kRank, r = e % kRank;
+                const int32_t tt = tsum[tok][r];
+                u[tok][r] = tok < M ? sbv[q] * (float)tt : 0.0f;
+                if (writer && rank != 0 && tok < M) fio.t[(p * M + tok) * kRank + r] = tt;
+            }
+        }
+        if (threadIdx.x < 16) {
+            int32_t s = 0;
+            for (int w = 0; w < W; ++w)
+                for (int gg = 0; gg < 4; ++gg) s += xs_part[w][16 * gg + threadIdx.x];
+            xsum[threadIdx.x] = s;
+        }
+        // (u and xsum are read after the first stage's barrier below)
+    } else {
+        // token scales and the LoRA down-projection: loaded now, stored to LDS after the
+        // activation loads below have been issued too
+        float tv[U], sbv[U];
+    #pragma unroll
+        for (int q = 0; q < U; ++q) {
+            const int e = threadIdx.x + q * W * kWave;
+            const int tok = e / kRank, r = e % kRank;
+            const bool live = e < 16 * kRank && tok < M;
+            if (rank != 0) {
+                const uint32_t m = opaque_mask(live);
+                tv[q] = (float)(int32_t)((uint32_t)t[(live ? tok : 0) * kRank + r] & m);
+                sbv[q] = __uint_as_float(__float_as_uint(s_b[r]) & m);
+            } else {
+                tv[q] = 0.0f;
+                sbv[q] = 0.0f;
+            }
+        }
+        const float sxv = __uint_as_float(__float_as_uint(s_x[threadIdx.x < M ? threadIdx.x : 0]) &
+                                          opaque_mask(threadIdx.x < M));
+
+        // Activations of token i in bit-plane order, for this lane's chunks.
+        int32_t xpart = 0;
+        const uint8_t* xrow = reinterpret_cast<const uint8_t*>(x_q) + (i < M ? (int64_t)i * K : 0);
+        const int64_t xlimit = i < M ? K : 0;
+    #pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int64_t q = ((int64_t)c * W + wave) * 4 + g;
+            const int64_t kb = 128 * q;
+            uint32_t nat[32];
+    #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint4 v = kFast ? load16_select(xrow, kb + 16 * e, kb + 16 * e < xlimit)
+                                      : load16_guarded<false>(xrow, kb + 16 * e, xlimit);
+                nat[4 * e + 0] = v.x;
+                nat[4 * e + 1] = v.y;
+                nat[4 * e + 2] = v.z;
+                nat[4 * e + 3] = v.w;
+            }
+    #pragma unroll
+            for (int e = 0; e < 32; ++e) xpart = byte_sum(nat[e], xpart);
+    #pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+    #pragma unroll
+                for (int jh = 0; jh < 2; ++jh) {
+                    uint32_t o0, o1, o2, o3;
+                    transpose4x4(nat[8 * qq + 0 + jh], nat[8 * qq + 2 + jh], nat[8 * qq + 4 + jh],
+                                 nat[8 * qq + 6 + jh], o0, o1, o2, o3);
+                    X[c][4 * jh + 0][qq] = (int)o0;
+                    X[c][4 * jh + 1][qq] = (int)o1;
+                    X[c][4 * jh + 2][qq] = (int)o2;
+                    X[c][4 * jh + 3][qq] = (int)o3;
+                }
+            }
+        }
+        // LoRA: u[tok][r] = s_B[r] * t[tok][r] (fp32), shared by every output row.
+    #pragma unroll
+        for (int q = 0; q < U; ++q) {
+            const int e = threadIdx.x + q * W * kWave;
+            if (e < 16 * kRank) u[e / kRank][e % kRank] = sbv[q] * tv[q];
+        }
+        if (threadIdx.x < 16) sxs[threadIdx.x] = sxv;
+        xs_part[wave][lane] = xpart;
+        for (int e = threadIdx.x; e < 2 * T * 16 * 20; e += W * kWave) (&red[0][0][0])[e] = 0;
+        lds_barrier();
+        if (threadIdx.x < 16) {
+            int32_t s = 0;
+            for (int w = 0; w < W; ++w)
+                for (int gg = 0; gg < 4; ++gg) s += xs_part[w][16 * gg + threadIdx.x];
+            xsum[threadIdx.x] = s;
+        }
+        // (xsum is read after the first stage's barrier below)
     }
-    if (threadIdx.x < 16) sxs[threadIdx.x] = sxv;
-    xs_part[wave][lane] = xpart;
-    for (int e = threadIdx.x; e < 2 * T * 16 * 20; e += W * kWave) (&red[0][0][0])[e] = 0;
-    lds_barrier();
-    if (threadIdx.x < 16) {
-        int32_t s = 0;
-        for (int w = 0; w < W; ++w)
-            for (int gg = 0; gg < 4; ++gg) s += xs_part[w][16 * gg + threadIdx.x];
-        xsum[threadIdx.x] = s;
-    }
-    // (xsum is read after the first stage's barrier below)
 
     // Outputs through buffer resources: dead elements store to an out-of-range offset.
     const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(y, (uint32_t)(M * N * 4));
@@ -322,25 +504,38 @@ template <int W, int C, int T>
 static hipError_t launch_gemv_wct(bool fast, const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
                                   const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
                                   const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                                  int64_t batch, hipStream_t stream) {
+                                  int64_t batch, const FusedIO* fio, hipStream_t stream) {
     const int64_t num_tiles = (N + 15) / 16;
     const int64_t num_stages = (num_tiles + T - 1) / T;
     // Large batches: about one resident round of groups (two 512-thread groups per CU
     // when a group is 8 waves), each over as many rows as it can hold, so the setup is
-    // paid once per group and no second round trails.  Otherwise ~8 groups per CU.
+    // paid once per group and no second round trails.  Otherwise ~8 groups per CU, or
+    // ~1 per CU for the fused variant, whose every group quantizes the tokens and
+    // reads all of W_B.
     const int64_t resident_wgs = 256 * (W >= 8 ? 2 : 16 / W);
-    const int64_t target_wgs = batch * num_stages >= 4 * resident_wgs ? resident_wgs : 2048;
+    const bool throughput = batch * num_stages >= 4 * resident_wgs;
+    const int64_t target_wgs = throughput ? resident_wgs : (fio ? 256 : 2048);
     const int64_t per_problem = (target_wgs + batch - 1) / batch;
     int stages_per_wg = (int)((num_stages + per_problem - 1) / per_problem);
     constexpr int kRowsCap = gemv_rows_cap(W, T);
     if (stages_per_wg * T * 16 > kRowsCap) stages_per_wg = kRowsCap / (T * 16);
     const dim3 grid((unsigned)((num_stages + stages_per_wg - 1) / stages_per_wg), (unsigned)batch);
-    if (fast) {
-        gemv_kernel<W, C, T, true><<<grid, W * kWave, 0, stream>>>(
-            x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, num_tiles, stages_per_wg);
+    // In the throughput regime the fused variant pays off only with one group per
+    // problem: every further group would quantize the tokens and read W_B again.
+    if (fio && throughput && grid.x > 1) return hipErrorNotSupported;
+    if (fio) {
+        if constexpr (C == 1) {
+            gemv_kernel<W, C, T, true, true><<<grid, W * kWave, 0, stream>>>(
+                x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, num_tiles, stages_per_wg, *fio);
+        } else {
+            return hipErrorNotSupported;
+        }
+    } else if (fast) {
+        gemv_kernel<W, C, T, true, false><<<grid, W * kWave, 0, stream>>>(
+            x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, num_tiles, stages_per_wg, FusedIO{});
     } else {
-        gemv_kernel<W, C, T, false><<<grid, W * kWave, 0, stream>>>(
-            x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, num_tiles, stages_per_wg);
+        gemv_kernel<W, C, T, false, false><<<grid, W * kWave, 0, stream>>>(
+            x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, num_tiles, stages_per_wg, FusedIO{});
     }
     return hipGetLastError();
 }
@@ -349,7 +544,7 @@ template <int W, int C>
 static hipError_t launch_gemv_wc(bool fast, const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
                                  const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
                                  const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                                 int64_t batch, hipStream_t stream) {
+                                 int64_t batch, const FusedIO* fio, hipStream_t stream) {
     // Few tiles overall (one decode call): one tile per stage spreads the rows over
     // the most CUs.  Many tiles (batched calls): four tiles per stage keep more
     // packed-sign loads in flight per wave.
@@ -357,21 +552,22 @@ static hipError_t launch_gemv_wc(bool fast, const int8_t* x_q, const float* s_x,
     const int64_t total_tiles = batch * ((N + 15) / 16);
     if (total_tiles <= 4096)
         return launch_gemv_wct<W, C, 1>(fast, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg,
-                                        batch, stream);
+                                        batch, fio, stream);
     return launch_gemv_wct<W, C, kTBig>(fast, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg,
-                                        batch, stream);
+                                        batch, fio, stream);
 }
 
-hipError_t launch_gemv(const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
-                       const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
-                       const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                       int64_t batch, hipStream_t stream) {
-    const int64_t RB = K / 8;
-    const int64_t NC = (RB + 15) / 16;  // 16-byte chunks per row
-    const bool fast = (RB % 16 == 0) && ((uintptr_t)w_bits % 16 == 0) && ((uintptr_t)x_q % 16 == 0);
+// Waves per group for rows of NC 16-byte chunks (zero: too long for the decode kernel).
+static int gemv_waves(int64_t NC) { return NC <= 4 ? 1 : NC <= 8 ? 2 : NC <= 16 ? 4 : NC <= 128 ? 8 : 0; }
+
+static hipError_t launch_gemv_any(bool fast, const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
+                                  const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
+                                  const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
+                                  int64_t batch, const FusedIO* fio, hipStream_t stream) {
+    const int64_t NC = (K / 8 + 15) / 16;  // 16-byte chunks per row
 #define DFSSM_GEMV(Wv, Cv) \
     return launch_gemv_wc<Wv, Cv>(fast, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, \
-                                  stream)
+                                  fio, stream)
     if (NC <= 4) DFSSM_GEMV(1, 1);
     if (NC <= 8) DFSSM_GEMV(2, 1);
     if (NC <= 16) DFSSM_GEMV(4, 1);
@@ -381,6 +577,37 @@ hipError_t launch_gemv(const int8_t* x_q, const float* s_x, int M, int64_t N, in
     if (NC <= 128) DFSSM_GEMV(8, 4);
 #undef DFSSM_GEMV
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv(const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
+                       const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
+                       const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
+                       int64_t batch, hipStream_t stream) {
+    const int64_t RB = K / 8;
+    const bool fast = (RB % 16 == 0) && ((uintptr_t)w_bits % 16 == 0) && ((uintptr_t)x_q % 16 == 0);
+    return launch_gemv_any(fast, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, nullptr,
+                           stream);
+}
+
+// Whether one launch can quantize, project down and run the scaffold product: whole
+// 128-k chunks, one chunk per lane (K <= 4096), at most 4 tokens, and the tokens'
+// codes within the group's LDS (M K <= 1024 x waves per group).
+bool decode_fused_supported(int64_t M, int64_t K) {
+    if (K % 128 != 0 || K > 4096 || M < 1 || M > 4) return false;
+    return M * K <= 1024 * gemv_waves(K / 128);
+}
+
+// hipErrorNotSupported (nothing launched) when the shape or the launch plan does not
+// suit the fused variant: the caller then takes the two-kernel form.
+hipError_t launch_decode_fused(const float* x, int M, int64_t N, int64_t K, const uint8_t* w_bits,
+                               const float* s_w, const int8_t* w_a, const float* s_a, const int8_t* w_b,
+                               const float* s_b, int rank, int8_t* x_q, float* s_x, int32_t* t, float* y,
+                               int32_t* acc_dbg, int64_t batch, hipStream_t stream) {
+    if (!decode_fused_supported(M, K) || (uintptr_t)w_bits % 16 != 0 || (uintptr_t)x % 16 != 0)
+        return hipErrorNotSupported;
+    const FusedIO fio{x, w_b, x_q, s_x, t};
+    return launch_gemv_any(true, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, &fio,
+                           stream);
 }
 
 }  // namespace dfssm

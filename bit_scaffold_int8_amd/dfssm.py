@@ -21,7 +21,8 @@ DFSSM_ERR_HIP = 3
 EXPORTED = ("dfssm_status_string", "dfssm_version", "dfssm_quantize_act", "dfssm_lora_down",
             "dfssm_lora_down_strided_batched", "dfssm_quantize_lora_down",
             "dfssm_quantize_lora_down_strided_batched", "dfssm_scaffold_lora_gemm",
-            "dfssm_scaffold_lora_gemm_strided_batched")
+            "dfssm_scaffold_lora_gemm_strided_batched", "dfssm_scaffold_lora_forward",
+            "dfssm_scaffold_lora_forward_strided_batched")
 
 
 class DfssmError(RuntimeError):
@@ -47,6 +48,9 @@ def _load():
         "dfssm_quantize_lora_down_strided_batched": [P, i64, i64, P, i32, P, P, P, i64, P],
         "dfssm_scaffold_lora_gemm": [P, P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P],
         "dfssm_scaffold_lora_gemm_strided_batched": [P, P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, i64, P],
+        "dfssm_scaffold_lora_forward": [P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P, P, P, P],
+        "dfssm_scaffold_lora_forward_strided_batched": [P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P, P, P,
+                                                        i64, P],
     }
     for name, argtypes in sigs.items():
         f = getattr(lib, name)
@@ -149,3 +153,25 @@ def dfssm_scaffold_lora_gemm_strided_batched(x_q, s_x, w_bits, s_w, w_a, s_a, s_
     rank = 0 if w_a is None else int(w_a.shape[2])
     _call("dfssm_scaffold_lora_gemm_strided_batched", _ptr(x_q), _ptr(s_x), M, N, K, _ptr(w_bits), _ptr(s_w),
           _ptr(w_a), _ptr(s_a), _ptr(s_b), _ptr(t), rank, _ptr(y), _ptr(acc_dbg), B, _stream(stream))
+
+
+def dfssm_scaffold_lora_forward(x, w_bits, s_w, w_a, s_a, w_b, s_b, x_q, s_x, t, y, acc_dbg=None,
+                                stream=None) -> None:
+    """The whole projection in one call: x fp32 [M, K] -> x_q, s_x, t and y [M, N]
+    (LoRA operands all None for rank 0)."""
+    M, K = x.shape
+    N = w_bits.shape[0]
+    rank = 0 if w_a is None else int(w_a.shape[1])
+    _call("dfssm_scaffold_lora_forward", _ptr(x), M, N, K, _ptr(w_bits), _ptr(s_w), _ptr(w_a), _ptr(s_a),
+          _ptr(w_b), _ptr(s_b), rank, _ptr(x_q), _ptr(s_x), _ptr(t), _ptr(y), _ptr(acc_dbg), _stream(stream))
+
+
+def dfssm_scaffold_lora_forward_strided_batched(x, w_bits, s_w, w_a, s_a, w_b, s_b, x_q, s_x, t, y,
+                                                acc_dbg=None, stream=None) -> None:
+    """Batched form of dfssm_scaffold_lora_forward: every operand with a leading [B]."""
+    B, M, K = x.shape
+    N = w_bits.shape[1]
+    rank = 0 if w_a is None else int(w_a.shape[2])
+    _call("dfssm_scaffold_lora_forward_strided_batched", _ptr(x), M, N, K, _ptr(w_bits), _ptr(s_w), _ptr(w_a),
+          _ptr(s_a), _ptr(w_b), _ptr(s_b), rank, _ptr(x_q), _ptr(s_x), _ptr(t), _ptr(y), _ptr(acc_dbg), B,
+          _stream(stream))

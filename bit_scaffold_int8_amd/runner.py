@@ -83,6 +83,12 @@ class DeviceProjections:
         self.quantize_lora_down(stream)
         self.gemm(stream, debug)
 
+    # ---- the one-call form (one launch at decode shapes)
+    def forward_one_call(self, stream=None, debug: bool = True):
+        dfssm.dfssm_scaffold_lora_forward_strided_batched(
+            self.x, self.w_bits, self.s_w, self.w_a, self.s_a, self.w_b, self.s_b, self.x_q, self.s_x, self.t,
+            self.y, self.acc_dbg if debug else None, stream)
+
     # ---- the unfused entry points, problem by problem (single-problem API)
     def forward_unfused(self, stream=None, debug: bool = True):
         for b in range(self.B):

@@ -16,10 +16,12 @@
  *   y[m][n]   = s_x[m] * ( s_w[n] * acc[m][n]
  *                          + s_A[n] * sum_r W_A[n][r] * s_B[r] * t[m][r] )   (fp32)
  *
- * A forward step is two calls: dfssm_quantize_lora_down (x -> x_q, s_x, t) and
- * dfssm_scaffold_lora_gemm (x_q, s_x, t -> y).  The LoRA down-projection t is a
- * reduction over all of K that every output needs, so it is produced before the
- * main kernel, which then runs without any cross-workgroup dependency.
+ * A forward step is one call, dfssm_scaffold_lora_forward (x -> x_q, s_x, t, y), or
+ * two: dfssm_quantize_lora_down (x -> x_q, s_x, t) and dfssm_scaffold_lora_gemm
+ * (x_q, s_x, t -> y).  The LoRA down-projection t is a reduction over all of K that
+ * every output needs; the two-call form produces it before the main kernel, which
+ * then runs without any cross-workgroup dependency, and the one-call form has every
+ * workgroup of a decode-shaped call compute it (and the codes) for itself.
  *
  * Data layout (all row-major, contiguous, device memory):
  *   x      fp32  [M][K]
@@ -144,6 +146,40 @@ dfssm_status dfssm_scaffold_lora_gemm_strided_batched(const int8_t* x_q, const f
                                                       const int32_t* t, int32_t rank,
                                                       float* y, int32_t* acc_dbg,
                                                       int64_t batch, hipStream_t stream);
+
+/*
+ * The whole projection in one call (technical summary sections 2B and 2C; the
+ * formulas above): x -> x_q, s_x, t and y, with the same results, bit for bit, as
+ * dfssm_quantize_lora_down followed by dfssm_scaffold_lora_gemm.
+ *   x                      fp32 [M][K], read
+ *   w_bits, s_w            the scaffold and its scale
+ *   w_a, s_a, w_b, s_b     the LoRA pair and its scales (rank 16), or rank 0 with
+ *                          all four (and t) NULL
+ *   x_q, s_x, t            written (the quantized tokens, their scales, t = W_B x_q)
+ *   y                      fp32 [M][N], written
+ *   acc_dbg                optional int32 [M][N] scaffold accumulators
+ * Decode shapes run as ONE kernel launch: K % 128 == 0, K <= 4096, M <= 4 and
+ * M*K <= 1024 * (waves per group: 1 for K <= 512, 2 for K <= 1024, 4 for K <= 2048,
+ * 8 up to 4096) -- e.g. M = 1, 2 at K = 4096 and K = 2048.  Every workgroup then
+ * quantizes the tokens and computes t itself; the first workgroup of each problem
+ * writes x_q, s_x and t.  Large batches that would spread one problem over several
+ * workgroups (which would each redo that work), and all other shapes, take the two
+ * kernels of the two-call form.
+ * Requirements and errors are the union of the two calls'.
+ */
+dfssm_status dfssm_scaffold_lora_forward(const float* x, int64_t M, int64_t N, int64_t K,
+                                         const uint8_t* w_bits, const float* s_w,
+                                         const int8_t* w_a, const float* s_a,
+                                         const int8_t* w_b, const float* s_b, int32_t rank,
+                                         int8_t* x_q, float* s_x, int32_t* t,
+                                         float* y, int32_t* acc_dbg, hipStream_t stream);
+dfssm_status dfssm_scaffold_lora_forward_strided_batched(const float* x, int64_t M, int64_t N, int64_t K,
+                                                         const uint8_t* w_bits, const float* s_w,
+                                                         const int8_t* w_a, const float* s_a,
+                                                         const int8_t* w_b, const float* s_b, int32_t rank,
+                                                         int8_t* x_q, float* s_x, int32_t* t,
+                                                         float* y, int32_t* acc_dbg,
+                                                         int64_t batch, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -116,3 +116,31 @@ def test_single_problem_gemm_rejects_like_batched():
     assert _raw("dfssm_scaffold_lora_gemm", A, A, 1, 16, 64, A, A, A, A, A, A, 8, A, None, None) == 2
     assert _raw("dfssm_lora_down", A, 1, 64, A, 0, A, None) == 2
     assert _raw("dfssm_quantize_lora_down", A, 1, 64, None, 16, A, A, A, None) == 1
+
+
+def _forward(**kw):
+    a = dict(x=A, M=1, N=16, K=128, w_bits=A, s_w=A, w_a=A, s_a=A, w_b=A, s_b=A, rank=16, x_q=A, s_x=A, t=A,
+             y=A, acc_dbg=None, batch=1)
+    a.update(kw)
+    return _raw("dfssm_scaffold_lora_forward_strided_batched", a["x"], a["M"], a["N"], a["K"], a["w_bits"],
+                a["s_w"], a["w_a"], a["s_a"], a["w_b"], a["s_b"], a["rank"], a["x_q"], a["s_x"], a["t"], a["y"],
+                a["acc_dbg"], a["batch"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), 1), (dict(x_q=None), 1), (dict(s_x=None), 1), (dict(w_bits=None), 1), (dict(s_w=None), 1),
+    (dict(y=None), 1), (dict(w_a=None), 1), (dict(s_a=None), 1), (dict(w_b=None), 1), (dict(s_b=None), 1),
+    (dict(t=None), 1),
+    (dict(M=0), 1), (dict(N=0), 1), (dict(K=0), 1), (dict(K=12), 1), (dict(batch=0), 1),
+    (dict(x=A + 4), 1), (dict(x_q=A + 4), 1), (dict(w_bits=A + 8), 1), (dict(w_a=A + 4), 1),
+    (dict(w_b=A + 8), 1), (dict(s_x=A + 2), 1), (dict(t=A + 1), 1), (dict(y=A + 2), 1), (dict(acc_dbg=A + 2), 1),
+    (dict(rank=8), 2), (dict(K=131072 + 8), 2), (dict(batch=65536), 2),
+])
+def test_forward_rejects(kw, want):
+    # the one-call form checks everything both calls of the two-call form check
+    assert _forward(**kw) == want
+
+
+def test_single_problem_forward_rejects_like_batched():
+    assert _raw("dfssm_scaffold_lora_forward", A, 1, 16, 12, A, A, A, A, A, A, 16, A, A, A, A, None, None) == 1
+    assert _raw("dfssm_scaffold_lora_forward", A, 1, 16, 128, A, A, A, A, A, A, 8, A, A, A, A, None, None) == 2
