@@ -10,7 +10,9 @@ arrays into it through ctypes.  What it computes follows the DF-SSM technical
 summary (gist.science), section 2B "Frozen Scaffold with LoRA Correction"
 (int8 rank-16 LoRA, W_A d_out x r, W_B r x d_in, per-channel/row scales) and
 section 2C "Optimized Inference Pipeline" (1-bit packed weights expanded to
-int8 for an int8 x int8 product); the numeric conventions the pages leave open
+int8 for an int8 x int8 product), and the int8 embedding / LM head with per-row
+scales (the summary's quantization and model-composition notes); the numeric
+conventions the pages leave open
 (absmax/127 scale, round half to even, LSB-first sign packing with bit 1 = +1,
 per-output-channel scaffold scale, fp32 output) are written at the top of the
 C file.
@@ -61,8 +63,11 @@ def _load():
     lib.oracle_lora_down.argtypes = [P, i64, i64, P, i32, P]
     lib.oracle_scaffold_lora_gemm.argtypes = [P, P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P, i32]
     lib.oracle_scaffold_lora_at.argtypes = [P, P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, i64, P, P, P]
+    lib.oracle_int8_rowscale_gemm.argtypes = [P, P, i64, i64, i64, P, P, P, P, i32]
+    lib.oracle_embedding_lookup.argtypes = [P, i64, P, P, i64, i64, P]
     for f in (lib.oracle_quantize_act, lib.oracle_scaffold_acc, lib.oracle_lora_down,
-              lib.oracle_scaffold_lora_gemm, lib.oracle_scaffold_lora_at):
+              lib.oracle_scaffold_lora_gemm, lib.oracle_scaffold_lora_at, lib.oracle_int8_rowscale_gemm,
+              lib.oracle_embedding_lookup):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -170,3 +175,34 @@ def scaffold_lora_at(x_q, s_x, w_bits, s_w, w_a, s_a, w_b, s_b, m_idx, n_idx):
         _ptr(t) if rank else None)
     _check(st, "scaffold_lora_at")
     return y, acc, t[:, :rank]
+
+
+def int8_rowscale_gemm(x_q, s_x, e, s_e, nthreads: int = 1):
+    """int8 LM head: acc[m, n] = sum_k E[n, k] x_q[m, k] (exact int32) and
+    y[m, n] = s_x[m] (s_e[n] acc[m, n]) (fp64, rounded once).  Returns (y, acc)."""
+    x_q = _c(x_q, np.int8)
+    s_x = _c(s_x, np.float32)
+    e = _c(e, np.int8)
+    s_e = _c(s_e, np.float32)
+    M, K = x_q.shape
+    N = e.shape[0]
+    assert e.shape == (N, K) and s_e.shape == (N,) and s_x.shape == (M,)
+    y = np.empty((M, N), np.float32)
+    acc = np.empty((M, N), np.int32)
+    _check(_load().oracle_int8_rowscale_gemm(_ptr(x_q), _ptr(s_x), M, N, K, _ptr(e), _ptr(s_e), _ptr(y),
+                                              _ptr(acc), int(nthreads)), "int8_rowscale_gemm")
+    return y, acc
+
+
+def embedding_lookup(tokens, e, s_e):
+    """Rows of the int8 embedding, dequantized: out[t, k] = s_e[id] E[id, k] (fp32);
+    ids outside [0, V) give zeros."""
+    tokens = _c(tokens, np.int32)
+    e = _c(e, np.int8)
+    s_e = _c(s_e, np.float32)
+    V, K = e.shape
+    T = tokens.shape[0]
+    out = np.empty((T, K), np.float32)
+    _check(_load().oracle_embedding_lookup(_ptr(tokens), T, _ptr(e), _ptr(s_e), V, K, _ptr(out)),
+           "embedding_lookup")
+    return out

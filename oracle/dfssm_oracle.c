@@ -199,3 +199,55 @@ int oracle_scaffold_lora_at(const int8_t* x_q, const float* s_x,
     }
     return ORACLE_OK;
 }
+
+/*
+ * int8 embedding / LM head (technical summary: the embedding and LM-head matrices
+ * are int8 with per-row scales; one tied matrix E [V][d] serves both).
+ *
+ * LM head, for M tokens against the V rows of E (here N = V, K = d):
+ *   acc[m][n] = sum_k E[n][k] * x_q[m][k]     (exact, int64, must fit int32)
+ *   y[m][n]   = fl32( s_x[m] * ( s_e[n] * acc[m][n] ) )   in fp64, rounded once
+ * with x_q, s_x the same per-token codes as above (oracle_quantize_act).
+ */
+int oracle_int8_rowscale_gemm(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
+                              const int8_t* e, const float* s_e, float* y, int32_t* acc_out, int32_t nthreads)
+{
+    if (M < 0 || N < 0 || K < 0) return ORACLE_ERR_ARG;
+    int status = ORACLE_OK;
+    for (int64_t m = 0; m < M; ++m) {
+        int overflow = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1) reduction(| : overflow)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; ++k)
+                s += (int64_t)e[n * K + k] * (int64_t)x_q[m * K + k];
+            if (s > INT32_MAX || s < INT32_MIN) { overflow = 1; continue; }
+            if (acc_out) acc_out[m * N + n] = (int32_t)s;
+            y[m * N + n] = (float)((double)s_x[m] * ((double)s_e[n] * (double)s));
+        }
+        if (overflow) status = ORACLE_ERR_OVERFLOW;
+    }
+    return status;
+}
+
+/*
+ * Embedding lookup: out[t][k] = fl32( s_e[id] * E[id][k] ) for id = tokens[t]; an id
+ * outside [0, V) gives a row of zeros.  (The product of an fp32 scale and an int8
+ * value is exact in fp64, so rounding it once to fp32 is the fp32 product.)
+ */
+int oracle_embedding_lookup(const int32_t* tokens, int64_t T, const int8_t* e, const float* s_e,
+                            int64_t V, int64_t K, float* out)
+{
+    if (T < 0 || V < 0 || K < 0) return ORACLE_ERR_ARG;
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t id = tokens[t];
+        for (int64_t k = 0; k < K; ++k) {
+            if (id < 0 || id >= V) {
+                out[t * K + k] = 0.0f;
+            } else {
+                out[t * K + k] = (float)((double)s_e[id] * (double)e[id * K + k]);
+            }
+        }
+    }
+    return ORACLE_OK;
+}

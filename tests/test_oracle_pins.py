@@ -218,3 +218,79 @@ def test_rejects_bad_arguments():
     # K must be a multiple of 8: the C side refuses K = 12
     with pytest.raises(RuntimeError):
         oracle.scaffold_acc(np.zeros((1, 12), np.int8), np.zeros((1, 1), np.uint8))
+
+
+# ------------------------------------------------------------------ int8 embedding / LM head
+
+def test_lm_head_hand_worked_example():
+    with open(os.path.join(GOLDEN, "lm_head_hand_worked.json")) as fh:
+        g = json.load(fh)
+    x = np.array(g["x"], np.float32)
+    e = np.array(g["e"], np.int8)
+    s_e = np.array(g["s_e"], np.float32)
+    x_q, s_x = oracle.quantize_act(x)
+    assert np.array_equal(s_x, np.array(g["expect_s_x"], np.float32))
+    assert np.array_equal(x_q, np.array(g["expect_x_q"], np.int8))
+    y, acc = oracle.int8_rowscale_gemm(x_q, s_x, e, s_e)
+    assert np.array_equal(acc, np.array(g["expect_acc"], np.int32))
+    assert np.array_equal(y, np.array(g["expect_y"], np.float32))
+    out = oracle.embedding_lookup(np.array(g["lookup_ids"], np.int32), e, s_e)
+    assert np.array_equal(out, np.array(g["expect_lookup"], np.float32))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 50, 64), (3, 37, 136), (16, 20, 520)])
+def test_lm_head_matches_fp64_blas(M, N, K):
+    # acc against numpy's int64 matrix product; y against the dequantized fp64 product
+    # sum_k (s_x x_q) (s_e E), which associates the scales differently
+    rng = np.random.default_rng(500 + M)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    e = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    s_e = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    x_q, s_x = oracle.quantize_act(x)
+    y, acc = oracle.int8_rowscale_gemm(x_q, s_x, e, s_e, nthreads=2)
+    assert np.array_equal(acc.astype(np.int64), x_q.astype(np.int64) @ e.astype(np.int64).T)
+    X = s_x.astype(np.float64)[:, None] * x_q.astype(np.float64)
+    E = s_e.astype(np.float64)[:, None] * e.astype(np.float64)
+    Y = X @ E.T
+    mag = np.abs(X) @ np.abs(E).T
+    ulp = np.spacing(np.abs(Y).astype(np.float32)).astype(np.float64)
+    assert (np.abs(y.astype(np.float64) - Y) <= ulp + 1e-12 * mag).all()
+
+
+def test_lm_head_invariants():
+    rng = np.random.default_rng(41)
+    M, N, K = 2, 64, 200
+    x_q = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    s_x = rng.uniform(0.01, 0.1, M).astype(np.float32)
+    e = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    s_e = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    y, acc = oracle.int8_rowscale_gemm(x_q, s_x, e, s_e)
+    # negating the matrix negates acc and y exactly (-128 never occurs in either operand)
+    y_n, acc_n = oracle.int8_rowscale_gemm(x_q, s_x, -e, s_e)
+    assert np.array_equal(acc_n, -acc) and np.array_equal(y_n, -y)
+    # permuting rows (with their scales) permutes the output columns
+    perm = rng.permutation(N)
+    y_p, acc_p = oracle.int8_rowscale_gemm(x_q, s_x, e[perm], s_e[perm])
+    assert np.array_equal(acc_p, acc[:, perm]) and np.array_equal(y_p, y[:, perm])
+    # a power-of-two row scale scales y exactly
+    y_2, _ = oracle.int8_rowscale_gemm(x_q, s_x, e, s_e * np.float32(4))
+    assert np.array_equal(y_2, y * np.float32(4))
+    # the largest accumulator: every operand at +-127
+    full = np.full((1, K), 127, np.int8)
+    _, acc_max = oracle.int8_rowscale_gemm(full, np.ones(1, np.float32), -full, np.ones(1, np.float32))
+    assert acc_max[0, 0] == -127 * 127 * K
+
+
+def test_embedding_lookup_properties():
+    rng = np.random.default_rng(43)
+    V, K = 30, 48
+    e = rng.integers(-127, 128, (V, K), dtype=np.int8)
+    ids = np.array([0, 29, 5, 5, -1, 30, 1 << 30], np.int32)
+    # unit scales return the int8 rows exactly; ids outside [0, V) give zeros
+    out = oracle.embedding_lookup(ids, e, np.ones(V, np.float32))
+    assert np.array_equal(out[:4], e[ids[:4]].astype(np.float32))
+    assert not out[4:].any()
+    # a scale 2^-j is an exact binary shift of every entry
+    s_e = np.float32(2.0) ** -rng.integers(0, 20, V).astype(np.float32)
+    out2 = oracle.embedding_lookup(ids[:4], e, s_e)
+    assert np.array_equal(out2, e[ids[:4]].astype(np.float64) * s_e[ids[:4]].astype(np.float64)[:, None])
