@@ -18,7 +18,8 @@ Extra keys report the per-call hipGraph latency, the prefill (M=2048) int8 MFMA
 throughput, the in_proj decode shapes (M = 1, 4, 16 over 256 rotated copies), the
 literal 64-copy figure (warm: 74.5 MB sits in the Infinity Cache), the 48-layer
 decode sweep as hipGraph replays (warm, and cold over three rotated weight sets),
-and two probes from the same run: the back-to-back dispatch interval of an empty
+the int8 LM head (vocabulary 50280 x width 2048, M = 1, 4, 16, cold and warm), and
+two probes from the same run: the back-to-back dispatch interval of an empty
 kernel and the device-to-device copy rate.
 """
 from __future__ import annotations
@@ -265,6 +266,51 @@ def decode_sweep_48l(torch, dev, replays):
             "note": "one hipGraph per token of 96 single-problem one-call projections; cold rotates 3 weight sets"}
 
 
+def head_bytes(M, N, K):
+    """Algorithmic bytes of one int8 LM-head call given the codes: E, s_e, x_q, s_x, y."""
+    return N * K + 4 * N + M * K + 4 * M + 4 * M * N
+
+
+def lm_head_decode(torch, dev, stream, steps, warmup):
+    """The int8 LM head (vocabulary 50280 x width 2048) at M = 1, 4, 16: one
+    dfssm_int8_rowscale_gemm launch per call.  Cold: three 103 MB weight copies (309 MB,
+    above the Infinity Cache) in rotation; warm: one copy replayed."""
+    import synth_inputs as si
+    from bit_scaffold_int8_amd import dfssm
+    cfg = si.CONFIGS["lm_head_decode_v50280_d2048"]
+    _, N, K = cfg["shapes"][0]
+    rng = np.random.default_rng(cfg["seed"])
+    copies = [si.draw_head(rng, 16, N, K) for _ in range(3)]
+    e = [torch.from_numpy(c.E).to(dev) for c in copies]
+    s_e = [torch.from_numpy(c.s_e).to(dev) for c in copies]
+    out = {"N": N, "K": K, "copies_cold": len(copies), "weight_bytes": N * K + 4 * N}
+    for M in (1, 4, 16):
+        x = torch.from_numpy(copies[0].x[:M]).to(dev)
+        x_q = torch.empty((M, K), dtype=torch.int8, device=dev)
+        s_x = torch.empty((M,), dtype=torch.float32, device=dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        dfssm.dfssm_quantize_act(x, x_q, s_x, stream)
+        it = iter(range(10 ** 9))
+
+        def cold():
+            c = next(it) % len(copies)
+            dfssm.dfssm_int8_rowscale_gemm(x_q, s_x, e[c], s_e[c], y, None, stream)
+
+        def warm():
+            dfssm.dfssm_int8_rowscale_gemm(x_q, s_x, e[0], s_e[0], y, None, stream)
+        for _ in range(warmup):
+            cold()
+        torch.cuda.synchronize()
+        cold_ms = time_events(torch, cold, 3 * steps, stream)
+        warm_ms = time_events(torch, warm, steps, stream)
+        b = head_bytes(M, N, K)
+        out[f"M{M}"] = {"cold_us": round(cold_ms * 1e3, 2), "cold_GBps": round(b / (cold_ms * 1e-3) / 1e9, 1),
+                        "cold_frac_of_hbm_peak": round(b / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "warm_us": round(warm_ms * 1e3, 2), "warm_GBps": round(b / (warm_ms * 1e-3) / 1e9, 1)}
+    del e, s_e
+    return out
+
+
 def cpu_baseline(probs, seconds):
     """The oracle (as it stands) on host cores over rotated copies for ~`seconds`."""
     import oracle
@@ -442,6 +488,7 @@ def main():
             "note": "warm: 64 copies fit the 256 MB Infinity Cache"}
         out["in_proj_decode_k2048_n8512"] = in_proj_decode(torch, dev, stream, args.steps, args.warmup)
         out["decode_sweep_48l"] = decode_sweep_48l(torch, dev, 10)
+        out["lm_head_decode_v50280_d2048"] = lm_head_decode(torch, dev, stream, args.steps, args.warmup)
         out["probes"] = probes(torch, stream)
 
     if args.no_extras and args.copy_probe:

@@ -8,7 +8,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdfssm.so")
-SOURCES = ["api.hip", "quantize.hip", "lora_down.hip", "gemv.hip", "gemm_mfma.hip", "gemm_prefill.hip"]
+SOURCES = ["api.hip", "quantize.hip", "lora_down.hip", "gemv.hip", "gemm_mfma.hip", "gemm_prefill.hip",
+           "int8_head.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

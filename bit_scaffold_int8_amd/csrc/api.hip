@@ -28,6 +28,11 @@ hipError_t launch_decode_fused(const float* x, int M, int64_t N, int64_t K, cons
                                const float* s_w, const int8_t* w_a, const float* s_a, const int8_t* w_b,
                                const float* s_b, int rank, int8_t* x_q, float* s_x, int32_t* t, float* y,
                                int32_t* acc_dbg, int64_t batch, hipStream_t stream);
+bool int8_head_supported(int64_t M, int64_t K);
+hipError_t launch_int8_head(const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K, const int8_t* e,
+                            const float* s_e, float* y, int32_t* acc_dbg, int64_t batch, hipStream_t stream);
+hipError_t launch_embedding_lookup(const int32_t* tokens, int64_t T, const int8_t* e, const float* s_e, int64_t V,
+                                   int64_t K, float* out, hipStream_t stream);
 bool prefill_supported(int64_t M, int64_t N, int64_t K);
 int prefill_num_cfgs();
 hipError_t launch_gemm_prefill(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
@@ -167,6 +172,23 @@ dfssm_status forward_impl(const float* x, int64_t M, int64_t N, int64_t K, const
     return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, stream);
 }
 
+dfssm_status int8_head_impl(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K, const int8_t* e,
+                           const float* s_e, float* y, int32_t* acc_dbg, int64_t batch, hipStream_t stream) {
+    if (!x_q || !s_x || !e || !s_e || !y) return DFSSM_ERR_INVALID_ARG;
+    if (dfssm_status st = check_sizes(M, K, batch)) return st;
+    if (N <= 0 || N >= kMaxRows || (K % 16) != 0) return DFSSM_ERR_INVALID_ARG;
+    if (!aligned16(x_q) || !aligned4(s_x) || !aligned16(e) || !aligned4(s_e) || !aligned4(y) ||
+        !aligned4_or_null(acc_dbg))
+        return DFSSM_ERR_INVALID_ARG;
+    // one problem's matrix and outputs are addressed with 32-bit offsets (plus one
+    // stage of rows past N)
+    if ((N + 128) * K >= ((int64_t)1 << 31) || M * N * 4 >= ((int64_t)1 << 31)) return DFSSM_ERR_UNSUPPORTED;
+    if (!dfssm::int8_head_supported(M, K)) return DFSSM_ERR_UNSUPPORTED;
+    return dfssm::launch_int8_head(x_q, s_x, (int)M, N, K, e, s_e, y, acc_dbg, batch, stream) == hipSuccess
+               ? DFSSM_OK
+               : DFSSM_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -241,6 +263,28 @@ dfssm_status dfssm_scaffold_lora_forward_strided_batched(const float* x, int64_t
                                                          float* y, int32_t* acc_dbg, int64_t batch,
                                                          hipStream_t stream) {
     return forward_impl(x, M, N, K, w_bits, s_w, w_a, s_a, w_b, s_b, rank, x_q, s_x, t, y, acc_dbg, batch, stream);
+}
+
+dfssm_status dfssm_int8_rowscale_gemm(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
+                                      const int8_t* e, const float* s_e, float* y, int32_t* acc_dbg,
+                                      hipStream_t stream) {
+    return int8_head_impl(x_q, s_x, M, N, K, e, s_e, y, acc_dbg, 1, stream);
+}
+
+dfssm_status dfssm_int8_rowscale_gemm_strided_batched(const int8_t* x_q, const float* s_x, int64_t M, int64_t N,
+                                                      int64_t K, const int8_t* e, const float* s_e, float* y,
+                                                      int32_t* acc_dbg, int64_t batch, hipStream_t stream) {
+    return int8_head_impl(x_q, s_x, M, N, K, e, s_e, y, acc_dbg, batch, stream);
+}
+
+dfssm_status dfssm_embedding_lookup(const int32_t* tokens, int64_t T, const int8_t* e, const float* s_e, int64_t V,
+                                    int64_t K, float* out, hipStream_t stream) {
+    if (!tokens || !e || !s_e || !out) return DFSSM_ERR_INVALID_ARG;
+    if (T <= 0 || V <= 0 || K <= 0 || T >= kMaxRows) return DFSSM_ERR_INVALID_ARG;
+    if (!aligned4(tokens) || !aligned4(s_e) || !aligned4(out)) return DFSSM_ERR_INVALID_ARG;
+    if (V * K >= ((int64_t)1 << 40) || T * K >= ((int64_t)1 << 40)) return DFSSM_ERR_UNSUPPORTED;
+    return dfssm::launch_embedding_lookup(tokens, T, e, s_e, V, K, out, stream) == hipSuccess ? DFSSM_OK
+                                                                                            : DFSSM_ERR_HIP;
 }
 
 }  // extern "C"

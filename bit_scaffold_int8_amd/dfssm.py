@@ -22,7 +22,8 @@ EXPORTED = ("dfssm_status_string", "dfssm_version", "dfssm_quantize_act", "dfssm
             "dfssm_lora_down_strided_batched", "dfssm_quantize_lora_down",
             "dfssm_quantize_lora_down_strided_batched", "dfssm_scaffold_lora_gemm",
             "dfssm_scaffold_lora_gemm_strided_batched", "dfssm_scaffold_lora_forward",
-            "dfssm_scaffold_lora_forward_strided_batched")
+            "dfssm_scaffold_lora_forward_strided_batched", "dfssm_int8_rowscale_gemm",
+            "dfssm_int8_rowscale_gemm_strided_batched", "dfssm_embedding_lookup")
 
 
 class DfssmError(RuntimeError):
@@ -51,6 +52,9 @@ def _load():
         "dfssm_scaffold_lora_forward": [P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P, P, P, P],
         "dfssm_scaffold_lora_forward_strided_batched": [P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P, P, P,
                                                         i64, P],
+        "dfssm_int8_rowscale_gemm": [P, P, i64, i64, i64, P, P, P, P, P],
+        "dfssm_int8_rowscale_gemm_strided_batched": [P, P, i64, i64, i64, P, P, P, P, i64, P],
+        "dfssm_embedding_lookup": [P, i64, P, P, i64, i64, P, P],
     }
     for name, argtypes in sigs.items():
         f = getattr(lib, name)
@@ -175,3 +179,26 @@ def dfssm_scaffold_lora_forward_strided_batched(x, w_bits, s_w, w_a, s_a, w_b, s
     _call("dfssm_scaffold_lora_forward_strided_batched", _ptr(x), M, N, K, _ptr(w_bits), _ptr(s_w), _ptr(w_a),
           _ptr(s_a), _ptr(w_b), _ptr(s_b), rank, _ptr(x_q), _ptr(s_x), _ptr(t), _ptr(y), _ptr(acc_dbg), B,
           _stream(stream))
+
+
+def dfssm_int8_rowscale_gemm(x_q, s_x, e, s_e, y, acc_dbg=None, stream=None) -> None:
+    """int8 LM head: y [M, N] = s_x (s_e (E x_q)) from x_q [M, K], s_x [M], e [N, K], s_e [N]."""
+    M, K = x_q.shape
+    N = e.shape[0]
+    _call("dfssm_int8_rowscale_gemm", _ptr(x_q), _ptr(s_x), M, N, K, _ptr(e), _ptr(s_e), _ptr(y), _ptr(acc_dbg),
+          _stream(stream))
+
+
+def dfssm_int8_rowscale_gemm_strided_batched(x_q, s_x, e, s_e, y, acc_dbg=None, stream=None) -> None:
+    """Batched form: x_q [B, M, K], s_x [B, M], e [B, N, K], s_e [B, N], y [B, M, N]."""
+    B, M, K = x_q.shape
+    N = e.shape[1]
+    _call("dfssm_int8_rowscale_gemm_strided_batched", _ptr(x_q), _ptr(s_x), M, N, K, _ptr(e), _ptr(s_e), _ptr(y),
+          _ptr(acc_dbg), B, _stream(stream))
+
+
+def dfssm_embedding_lookup(tokens, e, s_e, out, stream=None) -> None:
+    """out [T, K] = s_e[id] E[id] for the int32 ids `tokens` [T] (ids outside [0, V): zeros)."""
+    T = tokens.shape[0]
+    V, K = e.shape
+    _call("dfssm_embedding_lookup", _ptr(tokens), T, _ptr(e), _ptr(s_e), V, K, _ptr(out), _stream(stream))

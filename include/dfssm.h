@@ -181,6 +181,40 @@ dfssm_status dfssm_scaffold_lora_forward_strided_batched(const float* x, int64_t
                                                          float* y, int32_t* acc_dbg,
                                                          int64_t batch, hipStream_t stream);
 
+/*
+ * int8 LM head: the model's int8 embedding / LM-head matrix E [N][K] (N = vocabulary,
+ * K = model width) with one fp32 scale per row (technical summary: embedding and LM
+ * head quantized to int8 with per-row scaling), applied to M tokens' int8 codes:
+ *   acc[m][n] = sum_k E[n][k] * x_q[m][k]        (exact int32)
+ *   y[m][n]   = s_x[m] * (s_e[n] * acc[m][n])    (fp32)
+ * x_q, s_x are the tokens' per-token absmax codes (dfssm_quantize_act), the same as
+ * the projections take.  The pages leave the head's activation precision open; this
+ * int8 x int8 reading matches the rest of the int8 path.
+ *   x_q  int8 [M][K] (16-byte aligned), s_x fp32 [M]
+ *   e    int8 [N][K] (16-byte aligned), s_e fp32 [N]
+ *   y    fp32 [M][N], written; acc_dbg optional int32 [M][N] (verification aid)
+ * Requires K % 16 == 0 (DFSSM_ERR_INVALID_ARG otherwise); DFSSM_ERR_UNSUPPORTED for
+ * M > 16, K > 4096, or (N + 128) * K >= 2^31.  One kernel launch, bandwidth-bound
+ * (N K bytes per problem).  Batched form: operands of problem p at x_q + p*M*K,
+ * s_x + p*M, e + p*N*K, s_e + p*N, y + p*M*N, acc_dbg + p*M*N.
+ */
+dfssm_status dfssm_int8_rowscale_gemm(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
+                                      const int8_t* e, const float* s_e, float* y, int32_t* acc_dbg,
+                                      hipStream_t stream);
+dfssm_status dfssm_int8_rowscale_gemm_strided_batched(const int8_t* x_q, const float* s_x, int64_t M, int64_t N,
+                                                      int64_t K, const int8_t* e, const float* s_e, float* y,
+                                                      int32_t* acc_dbg, int64_t batch, hipStream_t stream);
+
+/*
+ * Embedding lookup from the same int8 matrix: out[t][k] = s_e[id] * E[id][k] (one fp32
+ * product) for id = tokens[t].  An id outside [0, V) gives a row of zeros (ids live in
+ * device memory, so they are not checked on the host).
+ *   tokens int32 [T], e int8 [V][K], s_e fp32 [V], out fp32 [T][K] (written)
+ * Requires T, V, K >= 1; V*K and T*K below 2^40.
+ */
+dfssm_status dfssm_embedding_lookup(const int32_t* tokens, int64_t T, const int8_t* e, const float* s_e,
+                                    int64_t V, int64_t K, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -82,7 +82,29 @@ def make_copies(M: int, N: int, K: int, n_outliers: int, seed: int, copies: int,
     return [draw_problem(rng, M, N, K, n_outliers, rank) for _ in range(copies)]
 
 
-# The five workloads: (name, list of (M, N, K, n_outliers), seed)
+@dataclass
+class HeadProblem:
+    """The int8 embedding / LM head's inputs: tokens' fp32 activations and the int8
+    matrix with its per-row scales (host numpy arrays)."""
+    x: np.ndarray      # float32 [M, K]
+    E: np.ndarray      # int8    [N, K]
+    s_e: np.ndarray    # float32 [N]
+
+
+def draw_head(rng: np.random.Generator, M: int, N: int, K: int) -> HeadProblem:
+    """Rows of per-row absmax int8 codes (uniform in [-127, 127]) with scales in
+    [1e-3, 1e-2], and N(0, 1) activations (the final hidden state of a token)."""
+    E = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    s_e = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    return HeadProblem(x, E, s_e)
+
+
+def make_head(M: int, N: int, K: int, seed: int) -> HeadProblem:
+    return draw_head(np.random.default_rng(seed), M, N, K)
+
+
+# The workloads: (name, list of (M, N, K, n_outliers), seed)
 CONFIGS = {
     "tiny_m1_k256_n512": dict(shapes=[(1, 512, 256, 2)], seed=0),
     "out_proj_decode_m1_k4096_n2048": dict(shapes=[(1, 2048, 4096, 2)], seed=1),
@@ -92,4 +114,6 @@ CONFIGS = {
     "decode_sweep_48l": dict(shapes=[(1, 8512, 2048, 0), (1, 2048, 4096, 0)], seed=3, layers=48),
     # prefill: 1 % outlier channels (round(0.01 K)) -> 20 at K 2048, 41 at K 4096
     "prefill_m2048": dict(shapes=[(2048, 8512, 2048, 20), (2048, 2048, 4096, 41)], seed=4),
+    # int8 LM head of the model: vocabulary 50280 x width 2048, decode token counts
+    "lm_head_decode_v50280_d2048": dict(shapes=[(1, 50280, 2048), (4, 50280, 2048), (16, 50280, 2048)], seed=5),
 }

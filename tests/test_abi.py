@@ -144,3 +144,31 @@ def test_forward_rejects(kw, want):
 def test_single_problem_forward_rejects_like_batched():
     assert _raw("dfssm_scaffold_lora_forward", A, 1, 16, 12, A, A, A, A, A, A, 16, A, A, A, A, None, None) == 1
     assert _raw("dfssm_scaffold_lora_forward", A, 1, 16, 128, A, A, A, A, A, A, 8, A, A, A, A, None, None) == 2
+
+
+def _head(**kw):
+    a = dict(x_q=A, s_x=A, M=1, N=16, K=64, e=A, s_e=A, y=A, acc_dbg=None, batch=1)
+    a.update(kw)
+    return _raw("dfssm_int8_rowscale_gemm_strided_batched", a["x_q"], a["s_x"], a["M"], a["N"], a["K"], a["e"],
+                a["s_e"], a["y"], a["acc_dbg"], a["batch"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x_q=None), 1), (dict(s_x=None), 1), (dict(e=None), 1), (dict(s_e=None), 1), (dict(y=None), 1),
+    (dict(M=0), 1), (dict(N=0), 1), (dict(K=0), 1), (dict(K=24), 1), (dict(batch=0), 1),
+    (dict(x_q=A + 8), 1), (dict(e=A + 4), 1), (dict(s_x=A + 2), 1), (dict(s_e=A + 1), 1), (dict(y=A + 2), 1),
+    (dict(acc_dbg=A + 2), 1),
+    (dict(M=17), 2), (dict(K=4096 + 16), 2), (dict(N=1 << 20, K=4096), 2), (dict(batch=65536), 2),
+])
+def test_int8_head_rejects(kw, want):
+    assert _head(**kw) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((None, 1, A, A, 10, 8, A), 1), ((A, 1, None, A, 10, 8, A), 1), ((A, 1, A, None, 10, 8, A), 1),
+    ((A, 1, A, A, 10, 8, None), 1), ((A, 0, A, A, 10, 8, A), 1), ((A, 1, A, A, 0, 8, A), 1),
+    ((A, 1, A, A, 10, 0, A), 1), ((A + 2, 1, A, A, 10, 8, A), 1), ((A, 1, A, A + 2, 10, 8, A), 1),
+    ((A, 1, A, A, 10, 8, A + 1), 1),
+])
+def test_embedding_lookup_rejects(args, want):
+    assert _raw("dfssm_embedding_lookup", *args, None) == want
