@@ -266,6 +266,24 @@ def decode_sweep_48l(torch, dev, replays):
             "note": "one hipGraph per token of 96 single-problem one-call projections; cold rotates 3 weight sets"}
 
 
+def mfma_probe():
+    """int8 MFMA rate this GPU sustains on given operand data (libdfssm_probe.so)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "bit_scaffold_int8_amd", "libdfssm_probe.so"))
+    lib.dfssm_probe_mfma_i8_tops.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.dfssm_probe_mfma_i8_tops.restype = ctypes.c_int
+    out = {}
+    for mode, name in enumerate(("b_01", "b_pm1", "b_random", "all_zero")):
+        v = ctypes.c_double(0.0)
+        rc = lib.dfssm_probe_mfma_i8_tops(mode, ctypes.byref(v))
+        if rc != 0:
+            raise RuntimeError(f"MFMA probe mode {mode} failed")
+        out[f"{name}_TOPS"] = round(v.value, 1)
+    out["note"] = ("v_mfma_i32_32x32x32_i8 back to back, 256 groups x 4 waves x 16 accumulators; "
+                   "A = activation-like codes, B = 0/1 bytes, +-1 bytes, random bytes; all_zero: A = B = 0")
+    return out
+
+
 def head_bytes(M, N, K):
     """Algorithmic bytes of one int8 LM-head call given the codes: E, s_e, x_q, s_x, y."""
     return N * K + 4 * N + M * K + 4 * M + 4 * M * N
@@ -472,6 +490,11 @@ def main():
                          "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
             del pp
         out["prefill_m2048"] = pre
+        # what the matrix cores sustain on this kind of data, for the prefill TOPS above
+        probe = mfma_probe()
+        out["mfma_i8_probe"] = probe
+        for name in pre:
+            pre[name]["frac_of_measured_01_rate"] = round(pre[name]["TOPS"] / probe["b_01_TOPS"], 4)
 
         # the literal 64-copy figure (74.5 MB: warm in the Infinity Cache)
         dp64 = DeviceProjections(

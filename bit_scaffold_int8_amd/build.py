@@ -1,4 +1,6 @@
-"""Compile the HIP sources under csrc/ into the in-tree shared library libdfssm.so (gfx950)."""
+"""Compile the HIP sources under csrc/ into the in-tree shared library libdfssm.so (gfx950),
+and the measurement probe (csrc/probe_mfma.hip) into libdfssm_probe.so, which only the
+benchmark loads."""
 from __future__ import annotations
 
 import os
@@ -8,6 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdfssm.so")
+PROBE_LIB = os.path.join(PKG, "libdfssm_probe.so")
+PROBE_SOURCES = ["probe_mfma.hip"]
 SOURCES = ["api.hip", "quantize.hip", "lora_down.hip", "gemv.hip", "gemm_mfma.hip", "gemm_prefill.hip",
            "int8_head.hip"]
 
@@ -37,12 +41,13 @@ def build(verbose: bool = False) -> str:
         subprocess.run(cmd, check=True)
         return obj
 
-    jobs = min(len(SOURCES), max(1, (os.cpu_count() or 1)))
+    jobs = min(len(SOURCES) + len(PROBE_SOURCES), max(1, (os.cpu_count() or 1)))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
-    subprocess.run(link, check=True)
-    os.replace(LIB + ".tmp", LIB)
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    for lib, lib_objs in ((LIB, objs[:len(SOURCES)]), (PROBE_LIB, objs[len(SOURCES):])):
+        link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *lib_objs, "-o", lib + ".tmp"]
+        subprocess.run(link, check=True)
+        os.replace(lib + ".tmp", lib)
     return LIB
 
 
