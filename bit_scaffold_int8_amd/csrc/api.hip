@@ -49,6 +49,7 @@ constexpr int64_t kGemvMaxK = 8 * 4 * 4 * 128;  // decode kernel: 8 waves x 4 la
 constexpr int64_t kMaxK = 131072;
 constexpr int64_t kMaxRows = (int64_t)1 << 31;
 constexpr int64_t kMaxBatch = 65535;  // problems ride gridDim.y
+constexpr int64_t kRankBytes = 16;     // one row of W_A (int8, rank 16)
 
 // Operands read with 16-byte vector loads (x, x_q, w_bits, w_a, w_b) must be 16-byte
 // aligned; scale vectors, t, y and acc_dbg only need their element alignment.
@@ -116,8 +117,10 @@ dfssm_status gemm_impl(const int8_t* x_q, const float* s_x, int64_t M, int64_t N
     }
     if (K > kMaxK) return DFSSM_ERR_UNSUPPORTED;
     hipError_t e;
-    // the decode kernel addresses one problem's signs and outputs with 32-bit offsets
-    const bool gemv_fits = N * (K / 8) < ((int64_t)1 << 31) && M * N * 4 < ((int64_t)1 << 31);
+    // the decode kernel addresses one problem's signs, LoRA rows and outputs with 32-bit
+    // offsets
+    const bool gemv_fits = N * (K / 8) < ((int64_t)1 << 31) && M * N * 4 < ((int64_t)1 << 31) &&
+                           N * kRankBytes < ((int64_t)1 << 31);
     if (M <= kMaxDecodeM && K <= kGemvMaxK && gemv_fits) {
         e = dfssm::launch_gemv(x_q, s_x, (int)M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch,
                                stream);
@@ -161,7 +164,8 @@ dfssm_status forward_impl(const float* x, int64_t M, int64_t N, int64_t K, const
     }
     if (K > kMaxK) return DFSSM_ERR_UNSUPPORTED;
     if (M * batch >= kMaxRows) return DFSSM_ERR_INVALID_ARG;
-    const bool gemv_fits = N * (K / 8) < ((int64_t)1 << 31) && M * N * 4 < ((int64_t)1 << 31);
+    const bool gemv_fits = N * (K / 8) < ((int64_t)1 << 31) && M * N * 4 < ((int64_t)1 << 31) &&
+                           N * kRankBytes < ((int64_t)1 << 31);
     if (gemv_fits && dfssm::decode_fused_supported(M, K)) {
         const hipError_t e = dfssm::launch_decode_fused(x, (int)M, N, K, w_bits, s_w, w_a, s_a, w_b, s_b, rank, x_q,
                                                         s_x, t, y, acc_dbg, batch, stream);

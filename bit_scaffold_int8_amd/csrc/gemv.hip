@@ -53,7 +53,11 @@ constexpr int gemv_rows_cap(int W, int T) { return (W >= 8 && T >= 4) ? 2048 : 1
 // kFused: quantize x and compute t in the setup (x_q, s_x, t are then outputs; needs
 // the 16-byte path, one chunk per lane, M <= 4 and M K <= 1024 W).
 template <int W, int C, int T, bool kFast, bool kFused>
-__global__ __launch_bounds__(W * kWave) void gemv_kernel(
+// One chunk per lane with 8 waves, or one tile per stage with 4: held to 128 registers
+// per lane, so that four waves share each SIMD (two 8-wave groups, or four 4-wave
+// groups, per CU); wider variants take what they need.
+__global__ __launch_bounds__(W * kWave)
+__attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && T == 1)) ? 4 : 1))) void gemv_kernel(
     const int8_t* __restrict__ x_q, const float* __restrict__ s_x, int M, int64_t N, int64_t K,
     const uint8_t* __restrict__ w_bits, const float* __restrict__ s_w,
     const int8_t* __restrict__ w_a, const float* __restrict__ s_a, const float* __restrict__ s_b,
@@ -77,8 +81,11 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     __shared__ int32_t red[2][T * 16][20];
     __shared__ int32_t xs_part[W][kWave];
     __shared__ int32_t xsum[16];
-    __shared__ float u[16][kRank];
-    __shared__ float sxs[16];
+    // u[tok][r] = s_B[r] t[tok][r], flat, plus one slot that absorbs the writes of
+    // threads past the 16 x 16 tile (a branch-free write keeps the compiler from sinking
+    // the t and s_B loads into a branch, where their use would wait for every load)
+    __shared__ float u[16 * kRank + 1];
+    __shared__ float sxs[17];  // slot 16 takes the discarded writes of lanes past 16
     // fused setup only: the tokens' codes, per-wave absmax partials, the t tile
     constexpr int kFusedMK = 1024 * W;  // largest M K the fused setup takes
     __shared__ __align__(16) uint32_t codes_lds[kFused ? kFusedMK / 4 : 1];
@@ -127,7 +134,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
         lane_off[c] = (int)((int64_t)i * RB + (16 * q < RB ? 16 * q : 0));
     }
     const int stage_bytes = (int)(T * 16 * RB);
-    auto load_stage = [&](int64_t st, uint4 (&wv)[T][C]) {
+    auto load_stage = [&](int64_t st, uint4 (&wv)[T][C]) __attribute__((always_inline)) {
 #pragma unroll
         for (int tt = 0; tt < T; ++tt) {
             if constexpr (kFast) {
@@ -155,27 +162,52 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     struct Stage {
         uint4 w[T][C];
     };
-    auto prefetch = [&](int64_t st, Stage& b) { load_stage(st, b.w); };
+    auto prefetch = [&](int64_t st, Stage& b) __attribute__((always_inline)) { load_stage(st, b.w); };
     Stage s0, s1, s2;
-    prefetch(st_begin, s0);  // every group has at least one stage
-    prefetch(st_begin + 1 < st_end ? st_begin + 1 : st_end - 1, s1);
+    auto prefetch_first_stages = [&]() __attribute__((always_inline)) {
+        prefetch(st_begin, s0);  // every group has at least one stage
+        prefetch(st_begin + 1 < st_end ? st_begin + 1 : st_end - 1, s1);
+    };
 
-    // the group's rows: W_A row, s_A and s_w into LDS (rank 0: zero LoRA operands)
+    // The group's rows: W_A row, s_A and s_w go to LDS (rank 0: zero LoRA operands).
+    // Loads complete in issue order, so anything issued ahead of the inputs the setup
+    // waits on would sit on its critical path: the setup issues its inputs first, then
+    // this thread's first row of epilogue operands (into registers) and the first two
+    // stages, and copies the operands to LDS only once its own work is done.
     const int64_t row0 = st_begin * T * 16;
     const int nrows = (int)((st_end - st_begin) * T * 16);
-    for (int r = threadIdx.x; r < nrows; r += W * kWave) {
+    auto row_clamped = [&](int r) __attribute__((always_inline)) {
         const int64_t n = row0 + r;
-        const bool live = n < N;
-        const int64_t nc = live ? n : N - 1;
-        sw_lds[r] = s_w[nc];
-        if (rank != 0) {
-            wa_lds[r] = *reinterpret_cast<const uint4*>(w_a + nc * kRank);
-            sa_lds[r] = s_a[nc];
-        } else {
-            wa_lds[r] = make_uint4(0u, 0u, 0u, 0u);
-            sa_lds[r] = 0.0f;
+        return n < N ? n : N - 1;
+    };
+    // (branch-free buffer loads: a load inside a branch makes the compiler copy its
+    // result at the join, which waits for every load issued before it; rank 0 gives
+    // the LoRA operands an empty range, so they read zero)
+    const __amdgpu_buffer_rsrc_t sw_rsrc = make_rsrc(s_w, (uint32_t)(N * 4));
+    const __amdgpu_buffer_rsrc_t wa_rsrc = make_rsrc(w_a, rank != 0 ? (uint32_t)(N * kRank) : 0u);
+    const __amdgpu_buffer_rsrc_t sa_rsrc = make_rsrc(s_a, rank != 0 ? (uint32_t)(N * 4) : 0u);
+    float r0_sw, r0_sa;
+    uint4 r0_wa;
+    auto load_first_row = [&]() __attribute__((always_inline)) {
+        const int nc = (int)row_clamped((int)threadIdx.x < nrows ? (int)threadIdx.x : nrows - 1);
+        r0_sw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sw_rsrc, 4 * nc, 0, 0));
+        r0_sa = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sa_rsrc, 4 * nc, 0, 0));
+        const v4i wa = __builtin_amdgcn_raw_buffer_load_b128(wa_rsrc, kRank * nc, 0, 0);
+        r0_wa = make_uint4((uint32_t)wa[0], (uint32_t)wa[1], (uint32_t)wa[2], (uint32_t)wa[3]);
+    };
+    auto store_rows = [&]() __attribute__((always_inline)) {
+        if ((int)threadIdx.x < nrows) {
+            sw_lds[threadIdx.x] = r0_sw;
+            wa_lds[threadIdx.x] = r0_wa;
+            sa_lds[threadIdx.x] = r0_sa;
         }
-    }
+        for (int r = threadIdx.x + W * kWave; r < nrows; r += W * kWave) {
+            const int64_t nc = row_clamped(r);
+            sw_lds[r] = s_w[nc];
+            wa_lds[r] = rank != 0 ? *reinterpret_cast<const uint4*>(w_a + nc * kRank) : make_uint4(0u, 0u, 0u, 0u);
+            sa_lds[r] = rank != 0 ? s_a[nc] : 0.0f;
+        }
+    };
 
     constexpr int U = (16 * kRank + W * kWave - 1) / (W * kWave);
     v4i X[C][8];
@@ -210,18 +242,25 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
         for (int e = 0; e < 8; ++e)
             wbv[e] = __builtin_amdgcn_raw_buffer_load_b128(
                 wb_rsrc, chunk_live ? (int)(i * K + 128 * qch + 16 * e) : kOffDead - 64, 0, 0);
+        const __amdgpu_buffer_rsrc_t sb_rsrc = make_rsrc(s_b, rank != 0 ? (uint32_t)(kRank * 4) : 0u);
         float sbv[U];
 #pragma unroll
         for (int q = 0; q < U; ++q) {
             const int e = threadIdx.x + q * NT;
-            sbv[q] = rank != 0 ? s_b[e % kRank] : 0.0f;
+            sbv[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sb_rsrc, 4 * (e % kRank), 0, 0));
         }
+        load_first_row();
+        prefetch_first_stages();
+        // every load above is issued before any of the work below waits on one
+        __builtin_amdgcn_sched_barrier(0);
 
-        // per-token absmax: per thread, per wave, then across waves through LDS
-        auto token_of = [&](int e) {
-            const int64_t f = (int64_t)e * NT + threadIdx.x;
-            const int64_t m = f * 4 / K;
-            return (int)(m < 3 ? m : 3);  // past the rows: zero values, any token
+        // per-token absmax: per thread, per wave, then across waves through LDS.  The
+        // token of float4 f is (4 f) / K, found by comparisons (M <= 4); past the rows
+        // the values are zero, so any token will do.
+        const int K32 = (int)K;
+        auto token_of = [&](int e) __attribute__((always_inline)) {
+            const int k4 = 4 * (e * NT + (int)threadIdx.x);
+            return (k4 >= K32 ? 1 : 0) + (k4 >= 2 * K32 ? 1 : 0) + (k4 >= 3 * K32 ? 1 : 0);
         };
         float am[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -240,18 +279,19 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
             }
         }
         lds_barrier();
-        float sc[4], inv[4], amx[4];
-        bool fast[4];
+        float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, inv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, amx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        bool fast[4] = {false, false, false, false};
 #pragma unroll
         for (int mm = 0; mm < 4; ++mm) {
-            float a = 0.0f;
-            if (mm < M)
+            if (mm < M) {  // uniform: two IEEE divisions per live token only
+                float a = 0.0f;
                 for (int w = 0; w < W; ++w) a = fmaxf(a, amax_part[w][mm]);
-            const RowScale rs = row_scale(a);
-            amx[mm] = a;
-            sc[mm] = a == 0.0f ? 0.0f : rs.s;
-            inv[mm] = rs.inv;
-            fast[mm] = rs.fast;
+                const RowScale rs = row_scale(a);
+                amx[mm] = a;
+                sc[mm] = a == 0.0f ? 0.0f : rs.s;
+                inv[mm] = rs.inv;
+                fast[mm] = rs.fast;
+            }
         }
 
         // codes into LDS (and x_q, s_x from the problem's first group)
@@ -328,7 +368,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
             if (e < 16 * kRank) {
                 const int tok = e / kRank, r = e % kRank;
                 const int32_t tt = tsum[tok][r];
-                u[tok][r] = tok < M ? sbv[q] * (float)tt : 0.0f;
+                u[tok * kRank + r] = tok < M ? sbv[q] * (float)tt : 0.0f;
                 if (writer && rank != 0 && tok < M) fio.t[(p * M + tok) * kRank + r] = tt;
             }
         }
@@ -338,51 +378,75 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
                 for (int gg = 0; gg < 4; ++gg) s += xs_part[w][16 * gg + threadIdx.x];
             xsum[threadIdx.x] = s;
         }
-        // (u and xsum are read after the first stage's barrier below)
+        store_rows();
+        // (u, xsum and the row operands are read after the first stage's barrier below)
     } else {
         // token scales and the LoRA down-projection: loaded now, stored to LDS after the
         // activation loads below have been issued too
+        // (buffer loads: t past M tokens and every LoRA operand at rank 0 read zero)
+        const __amdgpu_buffer_rsrc_t t_rsrc = make_rsrc(t, rank != 0 ? (uint32_t)(M * kRank * 4) : 0u);
+        const __amdgpu_buffer_rsrc_t sb_rsrc = make_rsrc(s_b, rank != 0 ? (uint32_t)(kRank * 4) : 0u);
         float tv[U], sbv[U];
-    #pragma unroll
+#pragma unroll
         for (int q = 0; q < U; ++q) {
             const int e = threadIdx.x + q * W * kWave;
             const int tok = e / kRank, r = e % kRank;
-            const bool live = e < 16 * kRank && tok < M;
-            if (rank != 0) {
-                const uint32_t m = opaque_mask(live);
-                tv[q] = (float)(int32_t)((uint32_t)t[(live ? tok : 0) * kRank + r] & m);
-                sbv[q] = __uint_as_float(__float_as_uint(s_b[r]) & m);
-            } else {
-                tv[q] = 0.0f;
-                sbv[q] = 0.0f;
-            }
+            const bool live = e < 16 * kRank;  // tokens past M fall past t's range
+            tv[q] = (float)(int32_t)__builtin_amdgcn_raw_buffer_load_b32(t_rsrc, live ? 4 * (tok * kRank + r) : kOffDead, 0, 0);
+            sbv[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sb_rsrc, 4 * r, 0, 0));
         }
-        const float sxv = __uint_as_float(__float_as_uint(s_x[threadIdx.x < M ? threadIdx.x : 0]) &
-                                          opaque_mask(threadIdx.x < M));
+        // token scales past M read zero (buffer range of M floats)
+        const float sxv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            make_rsrc(s_x, (uint32_t)(M * 4)), 4 * (threadIdx.x < 16 ? (int)threadIdx.x : 16), 0, 0));
 
-        // Activations of token i in bit-plane order, for this lane's chunks.
+        // Activations of token i in bit-plane order, for this lane's chunks.  With one
+        // chunk per lane its loads go out ahead of the first row's epilogue operands and
+        // the stage prefetches (32 registers); wider rows issue those first.
         int32_t xpart = 0;
         const uint8_t* xrow = reinterpret_cast<const uint8_t*>(x_q) + (i < M ? (int64_t)i * K : 0);
         const int64_t xlimit = i < M ? K : 0;
-    #pragma unroll
+        // One resource over all M rows (uniform, so it stays in scalar registers); lanes of
+        // tokens past M fall past its range and read zero, and so do chunks past the row's
+        // end (a far offset: they would otherwise read the next token's row).  K is a
+        // multiple of 128 on the 16-byte path, so a chunk is wholly in or out of the row.
+        const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(x_q, kFast ? (uint32_t)(M * K) : 0u);
+        const int xoff = kFast ? i * (int)K : 0;
+        if constexpr (C > 1) {
+            load_first_row();
+            prefetch_first_stages();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
         for (int c = 0; c < C; ++c) {
             const int64_t q = ((int64_t)c * W + wave) * 4 + g;
             const int64_t kb = 128 * q;
+            const int xb = kb < K ? xoff + (int)kb : 0x40000000;
             uint32_t nat[32];
-    #pragma unroll
+#pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint4 v = kFast ? load16_select(xrow, kb + 16 * e, kb + 16 * e < xlimit)
-                                      : load16_guarded<false>(xrow, kb + 16 * e, xlimit);
+                uint4 v;
+                if constexpr (kFast) {
+                    const v4i b = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xb + 16 * e, 0, 0);
+                    v = make_uint4((uint32_t)b[0], (uint32_t)b[1], (uint32_t)b[2], (uint32_t)b[3]);
+                } else {
+                    v = load16_guarded<false>(xrow, kb + 16 * e, xlimit);
+                }
                 nat[4 * e + 0] = v.x;
                 nat[4 * e + 1] = v.y;
                 nat[4 * e + 2] = v.z;
                 nat[4 * e + 3] = v.w;
             }
-    #pragma unroll
+            if constexpr (C == 1) {
+                __builtin_amdgcn_sched_barrier(0);  // the activation loads go out first
+                load_first_row();
+                prefetch_first_stages();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
             for (int e = 0; e < 32; ++e) xpart = byte_sum(nat[e], xpart);
-    #pragma unroll
+#pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-    #pragma unroll
+#pragma unroll
                 for (int jh = 0; jh < 2; ++jh) {
                     uint32_t o0, o1, o2, o3;
                     transpose4x4(nat[8 * qq + 0 + jh], nat[8 * qq + 2 + jh], nat[8 * qq + 4 + jh],
@@ -395,12 +459,12 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
             }
         }
         // LoRA: u[tok][r] = s_B[r] * t[tok][r] (fp32), shared by every output row.
-    #pragma unroll
+#pragma unroll
         for (int q = 0; q < U; ++q) {
             const int e = threadIdx.x + q * W * kWave;
-            if (e < 16 * kRank) u[e / kRank][e % kRank] = sbv[q] * tv[q];
+            u[e < 16 * kRank ? e : 16 * kRank] = sbv[q] * tv[q];
         }
-        if (threadIdx.x < 16) sxs[threadIdx.x] = sxv;
+        sxs[threadIdx.x < 16 ? threadIdx.x : 16] = sxv;
         xs_part[wave][lane] = xpart;
         for (int e = threadIdx.x; e < 2 * T * 16 * 20; e += W * kWave) (&red[0][0][0])[e] = 0;
         lds_barrier();
@@ -410,7 +474,8 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
                 for (int gg = 0; gg < 4; ++gg) s += xs_part[w][16 * gg + threadIdx.x];
             xsum[threadIdx.x] = s;
         }
-        // (xsum is read after the first stage's barrier below)
+        store_rows();
+        // (xsum and the row operands are read after the first stage's barrier below)
     }
 
     // Outputs through buffer resources: dead elements store to an out-of-range offset.
@@ -422,7 +487,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     // consume `cur`.  Branches below hold no global loads -- only LDS traffic, ALU work
     // and buffer stores -- so the compiler's waits stay partial across them and the
     // prefetched stages remain in flight.
-    auto run_stage = [&](int64_t st, Stage& cur, Stage& nxt2, int rb) {
+    auto run_stage = [&](int64_t st, Stage& cur, Stage& nxt2, int rb) __attribute__((always_inline)) {
         prefetch(st + 2 < st_end ? st + 2 : st_end - 1, nxt2);
         if (st >= st_end) return;  // uniform: stage past the group's range
 
@@ -478,7 +543,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
 #pragma unroll
                 for (int r = 0; r < kRank; ++r) {
                     const float a = (float)(int8_t)(words[r >> 2] >> (8 * (r & 3)));
-                    lora = fmaf(a, u[tok][r], lora);
+                    lora = fmaf(a, u[tok * kRank + r], lora);
                 }
                 const float inner = fmaf(sa, lora, sw * (float)acc_pm);
                 const int off = n < N ? (int)(((int64_t)tok * N + n) * 4) : kOffDead;
@@ -500,6 +565,25 @@ __global__ __launch_bounds__(W * kWave) void gemv_kernel(
     }
 }
 
+// Groups of one kernel instance that the GPU holds at once: the per-CU occupancy its
+// registers and LDS allow, times the CU count.  Taken once per instance.
+template <typename Kernel>
+static int64_t resident_groups(Kernel kernel, int threads) {
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    return (int64_t)per_cu * cus;
+}
+
+template <int W, int C, int T, bool kFast, bool kFused>
+static int64_t gemv_resident() {
+    static const int64_t n = resident_groups(gemv_kernel<W, C, T, kFast, kFused>, W * kWave);
+    return n;
+}
+
 template <int W, int C, int T>
 static hipError_t launch_gemv_wct(bool fast, const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
                                   const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
@@ -507,12 +591,17 @@ static hipError_t launch_gemv_wct(bool fast, const int8_t* x_q, const float* s_x
                                   int64_t batch, const FusedIO* fio, hipStream_t stream) {
     const int64_t num_tiles = (N + 15) / 16;
     const int64_t num_stages = (num_tiles + T - 1) / T;
-    // Large batches: about one resident round of groups (two 512-thread groups per CU
-    // when a group is 8 waves), each over as many rows as it can hold, so the setup is
-    // paid once per group and no second round trails.  Otherwise ~8 groups per CU, or
-    // ~1 per CU for the fused variant, whose every group quantizes the tokens and
-    // reads all of W_B.
-    const int64_t resident_wgs = 256 * (W >= 8 ? 2 : 16 / W);
+    // Large batches: one resident round of groups, each over as many rows as it can
+    // hold, so the setup is paid once per group and no second round trails.  Otherwise
+    // ~8 groups per CU, or ~1 per CU for the fused variant, whose every group quantizes
+    // the tokens and reads all of W_B.
+    int64_t resident_wgs;
+    if constexpr (C == 1) {
+        resident_wgs = fio ? gemv_resident<W, C, T, true, true>()
+                           : fast ? gemv_resident<W, C, T, true, false>() : gemv_resident<W, C, T, false, false>();
+    } else {
+        resident_wgs = fast ? gemv_resident<W, C, T, true, false>() : gemv_resident<W, C, T, false, false>();
+    }
     const bool throughput = batch * num_stages >= 4 * resident_wgs;
     const int64_t target_wgs = throughput ? resident_wgs : (fio ? 256 : 2048);
     const int64_t per_problem = (target_wgs + batch - 1) / batch;
