@@ -638,7 +638,9 @@ hipError_t launch_main(const prefill::Args& a, const Plan& p, int tail0, int tai
         return launch2<C0, T0>(a, s0, make_seg<T0>(a.M, p.n_split, a.N), batch, stream);
     if (p.tail_cfg >= 0 && p.tail_cfg == tail1)
         return launch2<C0, T1>(a, s0, make_seg<T1>(a.M, p.n_split, a.N), batch, stream);
-    return launch2<C0, C0>(a, s0, none, batch, stream);
+    // no tail, or a pinned one this main configuration has no instance for: every
+    // column on the main configuration
+    return launch2<C0, C0>(a, make_seg<C0>(a.M, 0, a.N), none, batch, stream);
 }
 
 }  // namespace

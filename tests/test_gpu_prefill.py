@@ -34,11 +34,13 @@ def test_prefill_config_parity(torch_cuda, monkeypatch, cfg, M, N, K):
     _check_full(si.make_problem(M, N, K, max(1, K // 100), seed=M * 31 + N * 7 + K + 5 * cfg))
 
 
-@pytest.mark.parametrize("main,tail", [(0, 1), (0, 2), (1, 2), (3, 5), (3, 6), (4, 6), (5, 6)])
+@pytest.mark.parametrize("main,tail", [(0, 1), (0, 2), (1, 2), (3, 5), (3, 6), (4, 5), (4, 6), (5, 6), (3, 4)])
 @pytest.mark.parametrize("M,N,K", [(130, 700, 1024), (64, 1000, 256), (2048, 8512, 512)])
 def test_prefill_main_plus_tail(torch_cuda, monkeypatch, main, tail, M, N, K):
     # whole tiles of one configuration and the remaining columns on a narrower one,
-    # in one launch (the plan the cost model picks for widths like 8512)
+    # in one launch (the plan the cost model picks for widths like 8512); (3, 4) pins
+    # a tail the main configuration has no instance for: every column then runs on
+    # the main configuration
     monkeypatch.setenv("DFSSM_PREFILL_CFG", str(main))
     monkeypatch.setenv("DFSSM_PREFILL_TAIL", str(tail))
     _check_full(si.make_problem(M, N, K, 3, seed=M + N + K + 10 * main + tail), nthreads=16)
