@@ -284,6 +284,27 @@ def mfma_probe():
     return out
 
 
+def barrier_probe():
+    """Microseconds per device-wide barrier round (libdfssm_probe.so): the cost a
+    persistent multi-layer decode kernel would pay between dependent projections."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "bit_scaffold_int8_amd", "libdfssm_probe.so"))
+    lib.dfssm_probe_grid_barrier_us.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.dfssm_probe_grid_barrier_us.restype = ctypes.c_int
+    out = {}
+    for groups in (256, 512):
+        for fenced in (0, 1):
+            v = ctypes.c_double(0.0)
+            rc = lib.dfssm_probe_grid_barrier_us(groups, fenced, ctypes.byref(v))
+            if rc != 0:
+                raise RuntimeError(f"barrier probe (groups {groups}, fenced {fenced}) failed: {rc}")
+            out[f"g{groups}_{'fenced' if fenced else 'coherent_ops'}_us"] = round(v.value, 2)
+    out["note"] = ("cooperative launch of 512-thread groups; per round: 64 floats written per group, a "
+                   "hierarchical counter barrier, 2048 floats read back; fenced = agent-scope release/acquire "
+                   "fences, coherent_ops = agent-scope atomic loads/stores of the data, no fences")
+    return out
+
+
 def head_bytes(M, N, K):
     """Algorithmic bytes of one int8 LM-head call given the codes: E, s_e, x_q, s_x, y."""
     return N * K + 4 * N + M * K + 4 * M + 4 * M * N
@@ -513,6 +534,7 @@ def main():
         out["decode_sweep_48l"] = decode_sweep_48l(torch, dev, 10)
         out["lm_head_decode_v50280_d2048"] = lm_head_decode(torch, dev, stream, args.steps, args.warmup)
         out["probes"] = probes(torch, stream)
+        out["grid_barrier_probe"] = barrier_probe()
 
     if args.no_extras and args.copy_probe:
         out["probes"] = probes(torch, stream)

@@ -1,5 +1,5 @@
 """Compile the HIP sources under csrc/ into the in-tree shared library libdfssm.so (gfx950),
-and the measurement probe (csrc/probe_mfma.hip) into libdfssm_probe.so, which only the
+and the measurement probes (csrc/probe_*.hip) into libdfssm_probe.so, which only the
 benchmark loads."""
 from __future__ import annotations
 
@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdfssm.so")
 PROBE_LIB = os.path.join(PKG, "libdfssm_probe.so")
-PROBE_SOURCES = ["probe_mfma.hip"]
+PROBE_SOURCES = ["probe_mfma.hip", "probe_barrier.hip"]
 SOURCES = ["api.hip", "quantize.hip", "lora_down.hip", "gemv.hip", "gemm_mfma.hip", "gemm_prefill.hip",
            "int8_head.hip"]
 
