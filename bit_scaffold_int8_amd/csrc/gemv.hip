@@ -53,11 +53,11 @@ constexpr int gemv_rows_cap(int W, int T) { return (W >= 8 && T >= 4) ? 2048 : 1
 // kFused: quantize x and compute t in the setup (x_q, s_x, t are then outputs; needs
 // the 16-byte path, one chunk per lane, M <= 4 and M K <= 1024 W).
 template <int W, int C, int T, bool kFast, bool kFused>
-// One chunk per lane with 8 waves, or one tile per stage with 4: held to 128 registers
-// per lane, so that four waves share each SIMD (two 8-wave groups, or four 4-wave
-// groups, per CU); wider variants take what they need.
+// One chunk per lane with 8 waves, or with 4 (except the fused 4-tile shape, which
+// needs more): held to 128 registers per lane, so that four waves share each SIMD (two
+// 8-wave groups, or four 4-wave groups, per CU); wider variants take what they need.
 __global__ __launch_bounds__(W * kWave)
-__attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && T == 1)) ? 4 : 1))) void gemv_kernel(
+__attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || !kFused))) ? 4 : 1))) void gemv_kernel(
     const int8_t* __restrict__ x_q, const float* __restrict__ s_x, int M, int64_t N, int64_t K,
     const uint8_t* __restrict__ w_bits, const float* __restrict__ s_w,
     const int8_t* __restrict__ w_a, const float* __restrict__ s_a, const float* __restrict__ s_b,
@@ -117,8 +117,6 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && T == 1)) ? 4 
     const int64_t num_stages = (num_tiles + T - 1) / T;
     const int64_t st_begin = (int64_t)blockIdx.x * stages_per_wg;
     const int64_t st_end = st_begin + stages_per_wg < num_stages ? st_begin + stages_per_wg : num_stages;
-    const int erow = threadIdx.x % (T * 16);
-    const int etok0 = threadIdx.x / (T * 16);
 
     // packed-sign loads of one stage: T tiles x C chunks, 16 bytes per lane.  The fast
     // path loads through a buffer resource over this problem's signs: offsets advance
@@ -526,6 +524,11 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && T == 1)) ? 4 
             }
         }
         lds_barrier();
+        // Epilogue element (row erow of the stage, tokens etok0 + q kTokStride): the
+        // thread-to-element map rotates by one wave per stage, so with few tokens the
+        // waves (and SIMDs) that carry the epilogue change from stage to stage.
+        const int rtid = (int)((threadIdx.x + (st % W) * kWave) % (W * kWave));
+        const int erow = rtid % (T * 16), etok0 = rtid / (T * 16);
         const int64_t n = st * T * 16 + erow;
         const int lrow = (int)(n - row0);
         const uint4 wa = wa_lds[lrow];
