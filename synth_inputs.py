@@ -104,6 +104,52 @@ def make_head(M: int, N: int, K: int, seed: int) -> HeadProblem:
     return draw_head(np.random.default_rng(seed), M, N, K)
 
 
+# Mamba-2 1.3B mixer sizes around the projections (in_proj width 8512 = 2 * 4096 +
+# 2 * 128 + 64): 64 heads of 64 channels, state size 128, one group, convolution width 4.
+MAMBA2_NHEADS, MAMBA2_HEADDIM, MAMBA2_DSTATE, MAMBA2_DCONV = 64, 64, 128, 4
+
+
+@dataclass
+class Mamba2Layer:
+    """One layer's decode-step parameters (host numpy arrays, float32)."""
+    conv_w: np.ndarray    # [conv_dim, 4]
+    conv_b: np.ndarray    # [conv_dim]
+    dt_bias: np.ndarray   # [nheads]
+    A_log: np.ndarray     # [nheads]
+    D: np.ndarray         # [nheads]
+    norm_w: np.ndarray    # [d_inner]
+
+
+def draw_mamba2_layer(rng: np.random.Generator, nheads: int = MAMBA2_NHEADS, headdim: int = MAMBA2_HEADDIM,
+                      d_state: int = MAMBA2_DSTATE) -> Mamba2Layer:
+    """Draw order: conv_w U(-0.5, 0.5), conv_b U(-0.5, 0.5), dt_bias U(-7, -2) (softplus
+    of it spans ~1e-3 .. 0.13), A_log U(0, log 16), D U(0.5, 1.5), norm_w 1 + 0.1 N(0, 1)."""
+    d_inner = nheads * headdim
+    conv_dim = d_inner + 2 * d_state
+    f32 = np.float32
+    conv_w = rng.uniform(-0.5, 0.5, (conv_dim, MAMBA2_DCONV)).astype(f32)
+    conv_b = rng.uniform(-0.5, 0.5, conv_dim).astype(f32)
+    dt_bias = rng.uniform(-7.0, -2.0, nheads).astype(f32)
+    A_log = rng.uniform(0.0, np.log(16.0), nheads).astype(f32)
+    D = rng.uniform(0.5, 1.5, nheads).astype(f32)
+    norm_w = (1.0 + 0.1 * rng.standard_normal(d_inner)).astype(f32)
+    return Mamba2Layer(conv_w, conv_b, dt_bias, A_log, D, norm_w)
+
+
+def draw_mamba2_inputs(rng: np.random.Generator, S: int, nheads: int = MAMBA2_NHEADS,
+                       headdim: int = MAMBA2_HEADDIM, d_state: int = MAMBA2_DSTATE):
+    """One step's (zxbcdt [S, 2 d_inner + 2 d_state + nheads], conv_state [S, conv_dim, 4],
+    ssm_state [S, nheads, headdim, d_state]) for S sequences, all float32: zxbcdt and the
+    convolution windows N(0, 1), the SSM state 0.1 N(0, 1)."""
+    d_inner = nheads * headdim
+    conv_dim = d_inner + 2 * d_state
+    f32 = np.float32
+    zxbcdt = rng.standard_normal((S, d_inner + conv_dim + nheads), dtype=f32)
+    conv_state = rng.standard_normal((S, conv_dim, MAMBA2_DCONV), dtype=f32)
+    ssm_state = (0.1 * rng.standard_normal((S, nheads, headdim, d_state), dtype=f32)).astype(f32)
+    return zxbcdt, conv_state, ssm_state
+
+
 # The workloads: (name, list of (M, N, K, n_outliers), seed)
 CONFIGS = {
     "tiny_m1_k256_n512": dict(shapes=[(1, 512, 256, 2)], seed=0),
@@ -116,4 +162,7 @@ CONFIGS = {
     "prefill_m2048": dict(shapes=[(2048, 8512, 2048, 20), (2048, 2048, 4096, 41)], seed=4),
     # int8 LM head of the model: vocabulary 50280 x width 2048, decode token counts
     "lm_head_decode_v50280_d2048": dict(shapes=[(1, 50280, 2048), (4, 50280, 2048), (16, 50280, 2048)], seed=5),
+    # the Mamba-2 step between the projections (conv shift register, SSM recurrence,
+    # gated RMS norm): 64 heads x 64 channels, state 128, at 1 and 64 sequences
+    "mamba2_decode_step": dict(sequences=[1, 64], seed=6),
 }
