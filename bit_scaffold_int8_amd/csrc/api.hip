@@ -33,6 +33,11 @@ hipError_t launch_int8_head(const int8_t* x_q, const float* s_x, int M, int64_t 
                             const float* s_e, float* y, int32_t* acc_dbg, int64_t batch, hipStream_t stream);
 hipError_t launch_embedding_lookup(const int32_t* tokens, int64_t T, const int8_t* e, const float* s_e, int64_t V,
                                    int64_t K, float* out, hipStream_t stream);
+bool mamba2_step_supported(int64_t nheads, int64_t headdim, int64_t d_state);
+hipError_t launch_mamba2_step(const float* zxbcdt, int64_t S, int nheads, const float* conv_in, float* conv_out,
+                              float* ssm_state, const float* conv_w, const float* conv_b, const float* dt_bias,
+                              const float* A_log, const float* D, const float* norm_w, float eps, float* out,
+                              hipStream_t stream);
 bool prefill_supported(int64_t M, int64_t N, int64_t K);
 int prefill_num_cfgs();
 hipError_t launch_gemm_prefill(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
@@ -289,6 +294,35 @@ dfssm_status dfssm_embedding_lookup(const int32_t* tokens, int64_t T, const int8
     if (V * K >= ((int64_t)1 << 40) || T * K >= ((int64_t)1 << 40)) return DFSSM_ERR_UNSUPPORTED;
     return dfssm::launch_embedding_lookup(tokens, T, e, s_e, V, K, out, stream) == hipSuccess ? DFSSM_OK
                                                                                             : DFSSM_ERR_HIP;
+}
+
+dfssm_status dfssm_mamba2_decode_step(const float* zxbcdt, int64_t S, int64_t nheads, int64_t headdim,
+                                      int64_t d_state, const float* conv_state_in, float* conv_state_out,
+                                      float* ssm_state, const float* conv_w, const float* conv_b,
+                                      const float* dt_bias, const float* A_log, const float* D,
+                                      const float* norm_w, float eps, float* out, hipStream_t stream) {
+    if (!zxbcdt || !conv_state_in || !conv_state_out || !ssm_state || !conv_w || !conv_b || !dt_bias || !A_log ||
+        !D || !norm_w || !out)
+        return DFSSM_ERR_INVALID_ARG;
+    if (S <= 0 || S > kMaxBatch || nheads <= 0 || headdim <= 0 || d_state <= 0) return DFSSM_ERR_INVALID_ARG;
+    if (!(eps >= 0.0f) || eps > 1e30f) return DFSSM_ERR_INVALID_ARG;
+    if (!aligned16(conv_state_in) || !aligned16(conv_state_out) || !aligned16(ssm_state) || !aligned16(conv_w) ||
+        !aligned16(norm_w) || !aligned16(out) || !aligned4(zxbcdt) || !aligned4(conv_b) || !aligned4(dt_bias) ||
+        !aligned4(A_log) || !aligned4(D))
+        return DFSSM_ERR_INVALID_ARG;
+    if (!dfssm::mamba2_step_supported(nheads, headdim, d_state)) return DFSSM_ERR_UNSUPPORTED;
+    const int64_t d_inner = nheads * headdim, conv_dim = d_inner + 2 * d_state;
+    auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
+        const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+        return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+    };
+    if (overlap(conv_state_in, S * conv_dim * 16, conv_state_out, S * conv_dim * 16) ||
+        overlap(out, S * d_inner * 4, zxbcdt, S * (d_inner + conv_dim + nheads) * 4))
+        return DFSSM_ERR_INVALID_ARG;
+    return dfssm::launch_mamba2_step(zxbcdt, S, (int)nheads, conv_state_in, conv_state_out, ssm_state, conv_w, conv_b,
+                                     dt_bias, A_log, D, norm_w, eps, out, stream) == hipSuccess
+               ? DFSSM_OK
+               : DFSSM_ERR_HIP;
 }
 
 }  // extern "C"

@@ -23,7 +23,7 @@ EXPORTED = ("dfssm_status_string", "dfssm_version", "dfssm_quantize_act", "dfssm
             "dfssm_quantize_lora_down_strided_batched", "dfssm_scaffold_lora_gemm",
             "dfssm_scaffold_lora_gemm_strided_batched", "dfssm_scaffold_lora_forward",
             "dfssm_scaffold_lora_forward_strided_batched", "dfssm_int8_rowscale_gemm",
-            "dfssm_int8_rowscale_gemm_strided_batched", "dfssm_embedding_lookup")
+            "dfssm_int8_rowscale_gemm_strided_batched", "dfssm_embedding_lookup", "dfssm_mamba2_decode_step")
 
 
 class DfssmError(RuntimeError):
@@ -55,6 +55,7 @@ def _load():
         "dfssm_int8_rowscale_gemm": [P, P, i64, i64, i64, P, P, P, P, P],
         "dfssm_int8_rowscale_gemm_strided_batched": [P, P, i64, i64, i64, P, P, P, P, i64, P],
         "dfssm_embedding_lookup": [P, i64, P, P, i64, i64, P, P],
+        "dfssm_mamba2_decode_step": [P, i64, i64, i64, i64, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P],
     }
     for name, argtypes in sigs.items():
         f = getattr(lib, name)
@@ -202,3 +203,15 @@ def dfssm_embedding_lookup(tokens, e, s_e, out, stream=None) -> None:
     T = tokens.shape[0]
     V, K = e.shape
     _call("dfssm_embedding_lookup", _ptr(tokens), T, _ptr(e), _ptr(s_e), V, K, _ptr(out), _stream(stream))
+
+
+def dfssm_mamba2_decode_step(zxbcdt, conv_state_in, conv_state_out, ssm_state, conv_w, conv_b, dt_bias, A_log, D,
+                             norm_w, eps, out, stream=None) -> None:
+    """Mamba-2 step for S sequences: zxbcdt [S, 2 d_inner + 2 d_state + nheads] (in_proj
+    output) -> out [S, d_inner] (out_proj input); conv_state_in -> conv_state_out
+    [S, conv_dim, 4]; ssm_state [S, nheads, headdim, d_state] updated in place."""
+    S = zxbcdt.shape[0]
+    _, nheads, headdim, d_state = ssm_state.shape
+    _call("dfssm_mamba2_decode_step", _ptr(zxbcdt), S, nheads, headdim, d_state, _ptr(conv_state_in),
+          _ptr(conv_state_out), _ptr(ssm_state), _ptr(conv_w), _ptr(conv_b), _ptr(dt_bias), _ptr(A_log), _ptr(D),
+          _ptr(norm_w), float(eps), _ptr(out), _stream(stream))

@@ -215,6 +215,39 @@ dfssm_status dfssm_int8_rowscale_gemm_strided_batched(const int8_t* x_q, const f
 dfssm_status dfssm_embedding_lookup(const int32_t* tokens, int64_t T, const int8_t* e, const float* s_e,
                                     int64_t V, int64_t K, float* out, hipStream_t stream);
 
+/*
+ * Mamba-2 decode step between in_proj and out_proj, for S sequences (technical
+ * summary, section 2C, Stateful Ops: the stateful shift register -- the causal
+ * convolution -- and the SSM recurrence; the arithmetic is the published Mamba-2
+ * single-token step, one group):
+ *   in_proj row = [z (d_inner) | xBC (conv_dim) | dt (nheads)],
+ *       d_inner = nheads * headdim, conv_dim = d_inner + 2 * d_state
+ *   window[c] <- [window[c][1..3], xBC[c]];  a = silu(sum_j conv_w[c][j] window[c][j] + conv_b[c])
+ *   x (nheads x headdim) | B (d_state) | C (d_state) = a
+ *   dt = softplus(dt + dt_bias) (identity above 20), dA = exp(-dt * exp(A_log))
+ *   state[h][p][n] = state[h][p][n] * dA[h] + (dt[h] * x[h][p]) * B[n]
+ *   y[h][p] = sum_n state[h][p][n] * C[n] + D[h] * x[h][p]
+ *   out = g / sqrt(mean(g^2) + eps) * norm_w,  g = y * silu(z)   (out_proj's input)
+ * Arguments (fp32, device memory; per sequence s the rows below are offset by s):
+ *   zxbcdt         [S][d_inner + conv_dim + nheads]   the in_proj output (read)
+ *   conv_state_in  [S][conv_dim][4]  the windows, oldest first (read; 16-byte aligned)
+ *   conv_state_out [S][conv_dim][4]  the advanced windows (written; 16-byte aligned;
+ *                  must not overlap conv_state_in: every group of a sequence reads the
+ *                  B and C windows that one of them rewrites)
+ *   ssm_state      [S][nheads][headdim][d_state]  updated in place (16-byte aligned)
+ *   conv_w [conv_dim][4] (16-byte aligned), conv_b [conv_dim], dt_bias, A_log, D [nheads],
+ *   norm_w [d_inner] (16-byte aligned), eps >= 0
+ *   out            [S][d_inner] (written; 16-byte aligned; must not overlap zxbcdt)
+ * Requires 1 <= S <= 65535; DFSSM_ERR_UNSUPPORTED unless headdim == 64, d_state == 128
+ * and 1 <= nheads <= 1024 (Mamba-2 1.3B: nheads 64).  Two kernel launches on `stream`.
+ * Non-finite inputs are a precondition violation (outputs undefined).
+ */
+dfssm_status dfssm_mamba2_decode_step(const float* zxbcdt, int64_t S, int64_t nheads, int64_t headdim,
+                                      int64_t d_state, const float* conv_state_in, float* conv_state_out,
+                                      float* ssm_state, const float* conv_w, const float* conv_b,
+                                      const float* dt_bias, const float* A_log, const float* D,
+                                      const float* norm_w, float eps, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

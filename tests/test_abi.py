@@ -172,3 +172,31 @@ def test_int8_head_rejects(kw, want):
 ])
 def test_embedding_lookup_rejects(args, want):
     assert _raw("dfssm_embedding_lookup", *args, None) == want
+
+
+def _mamba2(**kw):
+    far = 0x10000000  # distinct fake buffers far apart, so only the cases below overlap
+    a = dict(zxbcdt=A + 3 * far, S=1, nheads=64, headdim=64, d_state=128, conv_in=A, conv_out=A + far,
+             ssm=A, conv_w=A, conv_b=A, dt_bias=A, A_log=A, D=A, norm_w=A, eps=1e-5, out=A + 2 * far)
+    a.update(kw)
+    return _raw("dfssm_mamba2_decode_step", a["zxbcdt"], a["S"], a["nheads"], a["headdim"], a["d_state"],
+                a["conv_in"], a["conv_out"], a["ssm"], a["conv_w"], a["conv_b"], a["dt_bias"], a["A_log"], a["D"],
+                a["norm_w"], a["eps"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(zxbcdt=None), 1), (dict(conv_in=None), 1), (dict(conv_out=None), 1), (dict(ssm=None), 1),
+    (dict(conv_w=None), 1), (dict(conv_b=None), 1), (dict(dt_bias=None), 1), (dict(A_log=None), 1),
+    (dict(D=None), 1), (dict(norm_w=None), 1), (dict(out=None), 1),
+    (dict(S=0), 1), (dict(S=65536), 1), (dict(nheads=0), 1), (dict(headdim=0), 1), (dict(d_state=-1), 1),
+    (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1), (dict(eps=float("inf")), 1),
+    (dict(conv_in=A + 4), 1), (dict(conv_out=A + 0x10000000 + 8), 1), (dict(ssm=A + 4), 1), (dict(conv_w=A + 4), 1),
+    (dict(norm_w=A + 8), 1), (dict(out=A + 0x20000000 + 4), 1), (dict(zxbcdt=A + 2), 1), (dict(conv_b=A + 1), 1),
+    (dict(dt_bias=A + 2), 1), (dict(A_log=A + 2), 1), (dict(D=A + 2), 1),
+    (dict(conv_out=A), 1),                      # windows in and out overlap
+    (dict(conv_out=A + 4352 * 16 - 16), 1),     # ... by one window
+    (dict(out=A + 3 * 0x10000000 + 64), 1),     # out overlaps the in_proj output
+    (dict(headdim=32), 2), (dict(d_state=64), 2), (dict(nheads=1025), 2),
+])
+def test_mamba2_step_rejects(kw, want):
+    assert _mamba2(**kw) == want
