@@ -266,6 +266,97 @@ def decode_sweep_48l(torch, dev, replays):
             "note": "one hipGraph per token of 96 single-problem one-call projections; cold rotates 3 weight sets"}
 
 
+def mamba2_step_bytes(S, nheads=64, headdim=64, d_state=128):
+    """Algorithmic bytes of one Mamba-2 step: the SSM state and the convolution windows
+    read and written, the in_proj output read, the out_proj input written, and the
+    layer's parameters read once."""
+    d_inner = nheads * headdim
+    conv_dim = d_inner + 2 * d_state
+    per_seq = 2 * 4 * nheads * headdim * d_state + 2 * 16 * conv_dim + 4 * (d_inner + conv_dim + nheads) + 4 * d_inner
+    params = 16 * conv_dim + 4 * conv_dim + 3 * 4 * nheads + 4 * d_inner
+    return S * per_seq + params
+
+
+def mamba2_step_bench(torch, dev, iters):
+    """dfssm_mamba2_decode_step at 1, 64 and 512 sequences (the state is 2 MB per
+    sequence: 1 GB at 512, far above the Infinity Cache)."""
+    import synth_inputs as si
+    from bit_scaffold_int8_amd.runner import DeviceMamba2Layer
+    cfg = si.CONFIGS["mamba2_decode_step"]
+    rng = np.random.default_rng(cfg["seed"])
+    layer = si.draw_mamba2_layer(rng)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for S in (1, 64, 512):
+        zx, conv, ssm = si.draw_mamba2_inputs(rng, S)
+        m = DeviceMamba2Layer.from_host(layer, conv, ssm, device=dev)
+        zxd = torch.from_numpy(zx).to(dev)
+        for i in range(10):
+            m.step(zxd, i % 2, stream)
+        torch.cuda.synchronize()
+        ms = time_events(torch, lambda: (m.step(zxd, 0, stream), m.step(zxd, 1, stream)), iters, stream) / 2
+        nbytes = mamba2_step_bytes(S)
+        out[f"S{S}"] = {"us_per_step": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "bytes": nbytes}
+        del m, zxd
+    out["note"] = ("two launches per step (convolution + SSM recurrence + gate, then the gated RMS norm); "
+                   "bytes: state and windows read + written, in_proj output read, out_proj input written")
+    return out
+
+
+def decode_chain_48l(torch, dev, replays):
+    """The real decode dataflow at one sequence: per layer, in_proj (one-call) -> the
+    Mamba-2 step (2 launches) -> out_proj (one-call), each layer's in_proj reading the
+    previous out_proj's output (the residual add and the norm between layers are not
+    on the pages and are left out).  Two tokens per hipGraph (the convolution windows
+    alternate), warm: 172 MB of weights plus 101 MB of state, replayed back to back."""
+    import synth_inputs as si
+    from bit_scaffold_int8_amd.runner import DeviceProjections, DeviceMamba2Layer
+    cfg = si.CONFIGS["decode_sweep_48l"]
+    rng = np.random.default_rng(cfg["seed"] + 100)
+    layers = cfg["layers"]
+    (Mi, Ni, Ki, _), (Mo, No, Ko, _) = cfg["shapes"]
+    ins, outs, ssms = [], [], []
+    for _layer in range(layers):
+        ins.append(DeviceProjections.from_problems([si.draw_problem(rng, Mi, Ni, Ki, 0)], device=dev))
+        outs.append(DeviceProjections.from_problems([si.draw_problem(rng, Mo, No, Ko, 0)], device=dev))
+        layer = si.draw_mamba2_layer(rng)
+        _, conv, ssm = si.draw_mamba2_inputs(rng, 1)
+        ssms.append(DeviceMamba2Layer.from_host(layer, conv, ssm, device=dev))
+    for l in range(layers):
+        outs[l].x = ssms[l].out.view(1, 1, -1)
+        if l + 1 < layers:
+            ins[l + 1].x = outs[l].y
+    cs = torch.cuda.Stream()
+
+    def token(parity, stream):
+        for l in range(layers):
+            ins[l].forward_one_call(stream, debug=False)
+            ssms[l].step(ins[l].y.view(1, -1), parity, stream)
+            outs[l].forward_one_call(stream, debug=False)
+
+    with torch.cuda.stream(cs):
+        token(0, cs)
+        token(1, cs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        token(0, torch.cuda.current_stream())
+        token(1, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ms = time_events(torch, g.replay, replays, torch.cuda.current_stream()) / 2
+    finite = bool(torch.isfinite(outs[-1].y).all().item())
+    token_bytes = layers * (step_bytes(Mi, Ni, Ki) + step_bytes(Mo, No, Ko) + mamba2_step_bytes(1))
+    del g, ins, outs, ssms
+    return {"layers": layers, "launches_per_token": 4 * layers, "bytes_per_token": token_bytes,
+            "warm_us_per_token": round(ms * 1e3, 1), "warm_GBps": round(token_bytes / (ms * 1e-3) / 1e9, 1),
+            "last_output_finite": finite,
+            "note": "one hipGraph of two tokens; per layer in_proj (one-call), Mamba-2 step (2 launches), "
+                    "out_proj (one-call), each reading the previous one's output"}
+
+
 def mfma_probe():
     """int8 MFMA rate this GPU sustains on given operand data (libdfssm_probe.so)."""
     import ctypes
@@ -532,6 +623,8 @@ def main():
             "note": "warm: 64 copies fit the 256 MB Infinity Cache"}
         out["in_proj_decode_k2048_n8512"] = in_proj_decode(torch, dev, stream, args.steps, args.warmup)
         out["decode_sweep_48l"] = decode_sweep_48l(torch, dev, 10)
+        out["mamba2_decode_step"] = mamba2_step_bench(torch, dev, 20)
+        out["decode_chain_48l"] = decode_chain_48l(torch, dev, 10)
         out["lm_head_decode_v50280_d2048"] = lm_head_decode(torch, dev, stream, args.steps, args.warmup)
         out["probes"] = probes(torch, stream)
         out["grid_barrier_probe"] = barrier_probe()

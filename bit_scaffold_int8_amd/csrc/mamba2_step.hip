@@ -58,6 +58,16 @@ __global__ __launch_bounds__(kSsmThreads) void mamba2_ssm_kernel(
 
     __shared__ float xs[kPBlock], Bs[kDState], Cs[kDState];
 
+    // this thread's 8 state values (channel p of the block, values [8 q, 8 q + 8)) and the
+    // head's dt go out first: they do not depend on the convolution, so their latency
+    // overlaps its loads
+    const int p = tid / (kDState / 8), q = tid % (kDState / 8);
+    float4* const st = reinterpret_cast<float4*>(
+        ssm_state + ((s * nheads + h) * kHeadDim + pb * kPBlock + p) * (int64_t)kDState + 8 * q);
+    float4 h0 = st[0], h1 = st[1];
+    const float dt_raw = row[d_inner + conv_dim + h] + dt_bias[h];
+    const float a_log = A_log[h];
+
     // convolution: this group's 16 x channels, then B and C (272 channels)
     for (int idx = tid; idx < kPBlock + 2 * kDState; idx += kSsmThreads) {
         const int c = idx < kPBlock ? h * kHeadDim + pb * kPBlock + idx : d_inner + (idx - kPBlock);
@@ -81,17 +91,12 @@ __global__ __launch_bounds__(kSsmThreads) void mamba2_ssm_kernel(
         if (idx < kPBlock || blockIdx.x == 0) reinterpret_cast<float4*>(conv_out)[sc] = make_float4(win.y, win.z, win.w, xn);
     }
 
-    const float dt = softplus(row[d_inner + conv_dim + h] + dt_bias[h]);
-    const float dA = expf(-dt * expf(A_log[h]));
+    const float dt = softplus(dt_raw);
+    const float dA = expf(-dt * expf(a_log));
     __syncthreads();
 
-    // state: channel p of the block, values [8 q, 8 q + 8)
-    const int p = tid / (kDState / 8), q = tid % (kDState / 8);
     const float xp = xs[p];
     const float dtx = dt * xp;
-    float4* const st = reinterpret_cast<float4*>(
-        ssm_state + ((s * nheads + h) * kHeadDim + pb * kPBlock + p) * (int64_t)kDState + 8 * q);
-    float4 h0 = st[0], h1 = st[1];
     const float* const b = Bs + 8 * q;
     const float* const cc = Cs + 8 * q;
     h0.x = fmaf(h0.x, dA, dtx * b[0]);

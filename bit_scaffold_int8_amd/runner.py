@@ -100,3 +100,39 @@ class DeviceProjections:
                 None if not self.rank else self.w_a[b], None if not self.rank else self.s_a[b],
                 None if not self.rank else self.s_b[b], None if not self.rank else self.t[b], self.y[b],
                 None if (self.acc_dbg is None or not debug) else self.acc_dbg[b], stream)
+
+
+@dataclass
+class DeviceMamba2Layer:
+    """One layer's Mamba-2 step operands on the device, for S sequences: parameters,
+    the two convolution-window buffers (the step reads one and writes the other), the
+    SSM state (updated in place) and the out_proj input it writes."""
+    conv_w: torch.Tensor      # fp32 [conv_dim, 4]
+    conv_b: torch.Tensor      # fp32 [conv_dim]
+    dt_bias: torch.Tensor     # fp32 [nheads]
+    A_log: torch.Tensor       # fp32 [nheads]
+    D: torch.Tensor           # fp32 [nheads]
+    norm_w: torch.Tensor      # fp32 [d_inner]
+    windows: list             # two fp32 [S, conv_dim, 4]
+    ssm_state: torch.Tensor   # fp32 [S, nheads, headdim, d_state]
+    out: torch.Tensor         # fp32 [S, d_inner]
+    eps: float = 1e-5
+
+    @classmethod
+    def from_host(cls, layer, conv_state, ssm_state, device="cuda:0", eps: float = 1e-5):
+        """`layer` holds conv_w, conv_b, dt_bias, A_log, D, norm_w (numpy); conv_state
+        [S, conv_dim, 4] and ssm_state [S, nheads, headdim, d_state] the starting state."""
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        S, nheads, headdim, _ = ssm_state.shape
+        w0 = dev(conv_state)
+        return cls(conv_w=dev(layer.conv_w), conv_b=dev(layer.conv_b), dt_bias=dev(layer.dt_bias),
+                   A_log=dev(layer.A_log), D=dev(layer.D), norm_w=dev(layer.norm_w),
+                   windows=[w0, torch.empty_like(w0)], ssm_state=dev(ssm_state),
+                   out=torch.empty((S, nheads * headdim), dtype=torch.float32, device=device), eps=eps)
+
+    def step(self, zxbcdt, parity: int = 0, stream=None):
+        """One token: windows[parity] -> windows[1 - parity], state in place, out written."""
+        dfssm.dfssm_mamba2_decode_step(zxbcdt, self.windows[parity], self.windows[1 - parity], self.ssm_state,
+                                       self.conv_w, self.conv_b, self.dt_bias, self.A_log, self.D, self.norm_w,
+                                       self.eps, self.out, stream)
