@@ -147,3 +147,12 @@ def test_mamba2_step_eps_zero_and_large_inputs(torch_cuda):
     zx, conv, ssm = si.draw_mamba2_inputs(rng, 2)
     zx *= 30.0        # large pre-activations: silu saturates on both sides
     _check(layer, [zx], conv, ssm, eps=0.0)
+
+
+def test_mamba2_steps_33_sequences_5_heads(torch_cuda):
+    # two steps at 33 sequences of 5 heads
+    rng = np.random.default_rng(70)
+    layer = si.draw_mamba2_layer(rng, nheads=5)
+    zx0, conv, ssm = si.draw_mamba2_inputs(rng, 33, nheads=5)
+    zx1 = si.draw_mamba2_inputs(rng, 33, nheads=5)[0]
+    _check(layer, [zx0, zx1], conv, ssm)
