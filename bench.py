@@ -141,6 +141,8 @@ def parse():
     ap.add_argument("--prefill-iters", type=int, default=10)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMV traffic record from two rocprofv3 counter_collection.csv files")
+    ap.add_argument("--mamba2-only", action="store_true",
+                    help="only the Mamba-2 step legs and the copy probe (counter runs of the step kernels)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run the empty-kernel and copy probes even with --no-extras (counter calibration)")
     return ap.parse_args()
@@ -469,7 +471,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the projection is not sharded "
-              "across GPUs in this build.", file=sys.stderr)
+              "across GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -479,6 +481,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    if args.mamba2_only:
+        print(json.dumps({"mamba2_decode_step": mamba2_step_bench(torch, dev, args.steps),
+                          "probes": probes(torch, stream)}))
+        return
     M, N, K = 1, 2048, 4096
     R = args.copies
 
