@@ -257,7 +257,7 @@ def decode_sweep_48l(torch, dev, replays):
     cur = torch.cuda.current_stream()
     warm_ms = time_events(torch, graphs[0].replay, replays, cur)
     it = iter(range(10 ** 9))
-    cold_ms = time_events(torch, lambda: graphs[next(it) % 3].replay(), 3 * replays, cur)
+    cold_ms = time_events(torch, lambda: graphs[next(it) % 3].replay(), replays, cur)
     del graphs, sets
     return {"layers": cfg["layers"], "launches_per_token": 2 * cfg["layers"],
             "bytes_per_token": token_bytes,
@@ -265,7 +265,9 @@ def decode_sweep_48l(torch, dev, replays):
             "warm_GBps": round(token_bytes / (warm_ms * 1e-3) / 1e9, 1),
             "cold_us_per_token": round(cold_ms * 1e3, 1),
             "cold_GBps": round(token_bytes / (cold_ms * 1e-3) / 1e9, 1),
-            "note": "one hipGraph per token of 96 single-problem one-call projections; cold rotates 3 weight sets"}
+            "tokens_timed": replays,
+            "note": "one hipGraph per token of 96 single-problem one-call projections, replayed back to back; "
+                    "cold rotates 3 weight sets"}
 
 
 def mamba2_step_bytes(S, nheads=64, headdim=64, d_state=128):
@@ -354,7 +356,7 @@ def decode_chain_48l(torch, dev, replays):
     del g, ins, outs, ssms
     return {"layers": layers, "launches_per_token": 4 * layers, "bytes_per_token": token_bytes,
             "warm_us_per_token": round(ms * 1e3, 1), "warm_GBps": round(token_bytes / (ms * 1e-3) / 1e9, 1),
-            "last_output_finite": finite,
+            "last_output_finite": finite, "tokens_timed": 2 * replays,
             "note": "one hipGraph of two tokens; per layer in_proj (one-call), Mamba-2 step (2 launches), "
                     "out_proj (one-call), each reading the previous one's output"}
 
@@ -585,7 +587,7 @@ def main():
             torch.cuda.synchronize()
             g.replay()
             torch.cuda.synchronize()
-            graph_ms = time_events(torch, g.replay, 5, torch.cuda.current_stream())
+            graph_ms = time_events(torch, g.replay, 20, torch.cuda.current_stream())
             us_call = graph_ms * 1e3 / R
             per_call[name] = {"us_per_call": round(us_call, 3),
                               "GBps": round(step_bytes(M, N, K) / (us_call * 1e-6) / 1e9, 2),
@@ -628,9 +630,9 @@ def main():
             "gemv_GBps": round(64 * gemm_call_bytes(M, N, K) / (g64 * 1e-3) / 1e9, 1),
             "note": "warm: 64 copies fit the 256 MB Infinity Cache"}
         out["in_proj_decode_k2048_n8512"] = in_proj_decode(torch, dev, stream, args.steps, args.warmup)
-        out["decode_sweep_48l"] = decode_sweep_48l(torch, dev, 10)
+        out["decode_sweep_48l"] = decode_sweep_48l(torch, dev, 128)   # 128 tokens back to back
         out["mamba2_decode_step"] = mamba2_step_bench(torch, dev, 20)
-        out["decode_chain_48l"] = decode_chain_48l(torch, dev, 10)
+        out["decode_chain_48l"] = decode_chain_48l(torch, dev, 64)    # 64 two-token replays
         out["lm_head_decode_v50280_d2048"] = lm_head_decode(torch, dev, stream, args.steps, args.warmup)
         out["probes"] = probes(torch, stream)
         out["grid_barrier_probe"] = barrier_probe()
