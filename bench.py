@@ -464,6 +464,18 @@ def cpu_baseline(probs, seconds):
     return res
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where it is not readable)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -653,6 +665,8 @@ def main():
                       f"{res['single'][0]} problems in {res['single'][1]:.1f} s",
             "us_per_call": round(el / n * 1e6, 1),
             "single_thread_us_per_call": round(res["single"][1] / res["single"][0] * 1e6, 1),
+            "host_cpus": os.cpu_count(),
+            "cpu_model": cpu_model(),
         }
     out["setup_s"] = round(setup_s, 1)
     print(json.dumps(out), flush=True)
