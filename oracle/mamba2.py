@@ -25,7 +25,7 @@ softplus(v) = log(1 + exp(v)), returned as v itself for v > 20 (the threshold th
 reference implementation uses; the two differ there by < exp(-20) relative).
 silu(v) = v / (1 + exp(-v)).
 
-Parity status: pinned by ``tests/test_oracle_pins.py`` -- closed forms of one step
+Parity status: pinned by ``tests/test_oracle_mamba2_pins.py`` -- closed forms of one step
 from a zero state, pure decay with B = 0, a one-hot convolution that reproduces the
 shifted window, the recurrence against the quadratic (attention-like) form of the same
 SSM over several steps computed independently, and the norm's scale invariance.
