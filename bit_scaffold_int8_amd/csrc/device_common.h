@@ -117,6 +117,20 @@ __device__ __forceinline__ void store_i32(int32_t v, __amdgpu_buffer_rsrc_t r, i
     __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, r, byte_off, 0, 0);
 }
 
+// Device-scope stores (cache-policy bit SC1 of the buffer instruction's aux operand on
+// gfx950).  Such a store is written through the XCD's L2 rather than left dirty in it,
+// so a large output that every workgroup writes at the end of its tile drains while
+// the stores are issued, instead of in a write-back of the L2s when the kernel ends.
+// Measured on the prefill projections (64 MB and 16 MB of fp32 output) only; the
+// Mamba-2 state update, which rewrites what it reads, runs slower with it.
+constexpr int kAuxDeviceScope = 16;
+__device__ __forceinline__ void store_f32_dev(float v, __amdgpu_buffer_rsrc_t r, int byte_off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, kAuxDeviceScope);
+}
+__device__ __forceinline__ void store_i32_dev(int32_t v, __amdgpu_buffer_rsrc_t r, int byte_off) {
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, r, byte_off, 0, kAuxDeviceScope);
+}
+
 // A shift amount of 1 the optimizer cannot see (an empty asm statement with a scalar
 // register operand emits no instruction).  With a constant shift, InstCombine
 // re-associates a Horner chain (((a << 1) + b) << 1) + c into separate shifts and

@@ -33,11 +33,12 @@
 //  * Tails: every global access goes through a buffer resource; rows past M, columns
 //    past the tile and chunks past K or past the group's range read zero.
 //
-// Epilogue.  y = s_x (s_w acc + s_A sum_r W_A[n][r] s_B[r] t[m][r]).  The LoRA-up
-// product is a second, tiny contraction (rank 16) and runs on v_mfma_f32_32x32x16_bf16:
-// W_A is exact in bf16, and u = s_B t (fp32) is split exactly into three bf16 parts
-// (h + m + l, each the truncation of the remainder), so the products are exact and
-// only fp32 accumulation rounds.  Its output layout equals the int32 accumulator's,
+// Epilogue.  y = s_x (s_w acc + s_A sum_r W_A[n][r] s_B[r] t[m][r]), stored at device
+// scope (written through the L2, so the output drains while tiles still finish).
+// The LoRA-up product is a second, tiny contraction (rank 16) and runs on
+// v_mfma_f32_32x32x16_bf16: W_A is exact in bf16, and u = s_B t (fp32) is split
+// exactly into three bf16 parts (h + m + l, each the truncation of the remainder), so
+// the products are exact and only fp32 accumulation rounds.  Its output layout equals the int32 accumulator's,
 // so the scale epilogue combines them register by register.
 //
 // One launch can carry two tile configurations over two column ranges (a main part
@@ -478,8 +479,8 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
                 const int32_t acc_pm = 2 * acc[mb][nb][v] - rs[v];  // the +-1 sum
                 // without LoRA, sa = lo = 0 and the fma returns s_w acc unchanged
                 const float inner = fmaf(sa[nb], lo[v], sw[nb] * (float)acc_pm);
-                store_f32(sx[v] * inner, y_rsrc, off);
-                if constexpr (kDebug) store_i32(acc_pm, d_rsrc, off);
+                store_f32_dev(sx[v] * inner, y_rsrc, off);
+                if constexpr (kDebug) store_i32_dev(acc_pm, d_rsrc, off);
             }
         }
     }
