@@ -6,10 +6,13 @@
 // per-channel/row scales.  At many tokens the scaffold product is a dense int8
 // contraction, so it runs on v_mfma_i32_32x32x32_i8; nothing is materialized in memory.
 //
-// Work split.  A workgroup is 4 waves (one per SIMD) and owns a (32 MB) x (32 NB WNW)
-// output tile: WNW = 4 / KS waves side by side along N and KS groups along K
-// (split-K inside the workgroup, summed through LDS at the end).  Each wave keeps its
-// (32 MB) x (32 NB) partial tile in MB x NB accumulators of 16 registers (AGPRs).
+// Work split.  A workgroup is NW = 4 or 8 waves (one or two per SIMD) and owns a
+// (32 MB) x (32 NB WNW) output tile: WNW = NW / KS waves side by side along N and KS
+// groups along K (split-K inside the workgroup, summed through LDS at the end).  Each
+// wave keeps its (32 MB) x (32 NB) partial tile in MB x NB accumulators of 16
+// registers (AGPRs).  Some 4-wave configurations run two workgroups per CU, each with
+// half the register and LDS budget: the two drift apart, so one's epilogue stores and
+// the narrow tail groups overlap the other's MFMA work.
 //
 // Weights as 0/1.  A sign w = 2 b - 1 with bit b, so sum_k w x = 2 S - R with
 // S = sum_k b x (the MFMA product with 0/1 bytes) and R = sum_k x (the token's code
@@ -42,8 +45,8 @@
 // so the scale epilogue combines them register by register.
 //
 // One launch can carry two tile configurations over two column ranges (a main part
-// and a narrow tail), so that a width like 8512 = 16 x 512 + 320 fills the machine in
-// about one round instead of two.
+// and a narrow tail), so that a width like 8512 = 32 x 256 + 320 takes one round of
+// main tiles plus tail groups that run beside them, instead of two full rounds.
 #include "device_common.h"
 
 namespace dfssm {
@@ -61,9 +64,11 @@ constexpr int kLoadDead = 0x7ff00000;  // a load offset past every resource used
 constexpr int kRedBlocks = 8;          // accumulator blocks per split-K reduction phase
 constexpr int kColDead = 0x40000000;   // store offset added for columns past the range: past the y resource
 
-template <int MB_, int NB_, int KS_, int NW_ = 4>
+// OCC_ workgroups of the configuration share a CU (its register and LDS budgets are
+// split between them).
+template <int MB_, int NB_, int KS_, int NW_ = 4, int OCC_ = 1>
 struct Cfg {
-    static constexpr int MB = MB_, NB = NB_, KS = KS_, NW = NW_;
+    static constexpr int MB = MB_, NB = NB_, KS = KS_, NW = NW_, OCC = OCC_;
     static constexpr int WNW = NW / KS;                      // waves along N
     static constexpr int BM = 32 * MB, WN = 32 * NB, BN = WN * WNW;
     static constexpr int GS = kWave * WNW;                   // threads of one K group
@@ -77,11 +82,11 @@ struct Cfg {
     // area that reuses them
     static constexpr int kRowSumOff = KS * kGroupBytes > kRedBytes ? KS * kGroupBytes : kRedBytes;
     static constexpr int kLdsBytes = kRowSumOff + KS * BM * 4;
-    static_assert(NW == 4 || NW == 8, "one or two waves per SIMD");
+    static_assert((NW == 4 || NW == 8) && NW * OCC <= 8, "one or two waves per SIMD");
     static_assert(KS == 1 || KS == 2 || KS == 4, "waves split over K and N");
     static_assert(P * GS == BM * 8 && (P % 4 == 0 || 4 % P == 0), "code pieces split evenly over steps");
     static_assert(JB * GS == BN * kBlk, "sign pieces split evenly over threads");
-    static_assert(kLdsBytes <= 160 * 1024, "LDS");
+    static_assert(kLdsBytes * OCC <= 160 * 1024, "LDS");
 };
 
 // One part of a launch: a column range [n_begin, n_end) tiled by one configuration.
@@ -491,9 +496,9 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
 // (workgroups go to XCDs round-robin), so the code rows and sign columns one XCD reads
 // stay in its L2.
 template <class C0, class C1, bool kDebug>
-__global__ __launch_bounds__(C0::NW * kWave) __attribute__((amdgpu_waves_per_eu(C0::NW / 4, C0::NW / 4))) void
+__global__ __launch_bounds__(C0::NW * kWave) __attribute__((amdgpu_waves_per_eu(C0::NW / 4 * C0::OCC, C0::NW / 4 * C0::OCC))) void
 gemm_prefill_kernel(prefill::Args a, prefill::Seg seg0, prefill::Seg seg1) {
-    static_assert(C0::NW == C1::NW, "both parts of a launch use the same workgroup size");
+    static_assert(C0::NW == C1::NW && C0::OCC == C1::OCC, "both parts of a launch use the same workgroup shape");
     constexpr int kLds = C0::kLdsBytes > C1::kLdsBytes ? C0::kLdsBytes : C1::kLdsBytes;
     __shared__ __align__(16) uint8_t lds[kLds];
     {
@@ -536,14 +541,18 @@ using C4218 = Cfg<4, 2, 1, 8>;  // 128 x 512, two waves per SIMD
 using C4128 = Cfg<4, 1, 2, 8>;  // 128 x 128, split-K by 2, two waves per SIMD
 using C2128 = Cfg<2, 1, 2, 8>;  // 64 x 128, split-K by 2, two waves per SIMD (narrow parts)
 using C2148 = Cfg<2, 1, 4, 8>;  // 64 x 64, split-K by 4, two waves per SIMD (narrow parts)
+using C4214 = Cfg<4, 2, 1, 4, 2>;  // 128 x 256, two 4-wave groups per CU
+using C2124 = Cfg<2, 1, 2, 4, 2>;  // 64 x 64, split-K by 2, two 4-wave groups per CU (narrow parts)
 
 struct CfgInfo {
-    int bm, bn, ks, nw, wave_cols;
+    int bm, bn, ks, nw, wave_cols, occ;
 };
-constexpr CfgInfo kCfgs[] = {{128, 512, 1, 4, 128}, {128, 128, 2, 4, 64}, {128, 64, 2, 4, 32},
-                             {128, 512, 1, 8, 64},  {128, 128, 2, 8, 32}, {64, 128, 2, 8, 32},
-                             {64, 64, 4, 8, 32}};
-constexpr int kNumCfgs = 7;
+constexpr CfgInfo kCfgs[] = {{128, 512, 1, 4, 128, 1}, {128, 128, 2, 4, 64, 1}, {128, 64, 2, 4, 32, 1},
+                             {128, 512, 1, 8, 64, 1},  {128, 128, 2, 8, 32, 1}, {64, 128, 2, 8, 32, 1},
+                             {64, 64, 4, 8, 32, 1},    {128, 256, 1, 4, 64, 2}, {64, 64, 2, 4, 32, 2}};
+constexpr int kNumCfgs = 9;
+// The narrower configurations each one is instantiated with for a tail (-1: none).
+constexpr int kTails[kNumCfgs][2] = {{1, 2}, {2, -1}, {-1, -1}, {5, 6}, {5, 6}, {6, -1}, {-1, -1}, {8, -1}, {-1, -1}};
 constexpr int kNumCUs = 256;
 
 struct Plan {
@@ -556,56 +565,95 @@ int64_t tiles_of(int cfg, int64_t M, int64_t n_cols) {
     return ((M + c.bm - 1) / c.bm) * ((n_cols + c.bn - 1) / c.bn);
 }
 
+// Workgroups of configuration cfg the GPU holds at once.
+int64_t slots_of(int cfg) { return (int64_t)kNumCUs * kCfgs[cfg].occ; }
+
 // Modelled time of one part, in units of a 128 x 128 x 128 MFMA step of one SIMD:
-// rounds of one-workgroup-per-CU tiles times the steps of one SIMD (a chunk count
-// rounded up to the 4-chunk sign block), 10 % extra for the split-K hand-over, 15 %
-// less with two waves per SIMD (measured: their stalls overlap), and 60 % more for
-// 64-row tiles (half the MFMAs per expanded sign operand).
+// rounds of resident workgroups, each costing a fixed latency (prologue, epilogue,
+// launch: ~2.3 units, fitted to the measured cost of a short second round) plus the
+// steps of one SIMD (a chunk count rounded up to the 4-chunk sign block; the SIMD
+// serves one wave of each co-resident group), 10 % extra for the split-K hand-over,
+// 15 % less with two waves per SIMD (measured: their stalls overlap), and 60 % more
+// for 64-row tiles (half the MFMAs per expanded sign operand).
+constexpr double kRoundLatency = 2.3;
 double part_cost(int cfg, int64_t M, int64_t n_cols, int64_t K, int64_t batch, int64_t* wgs_out) {
     const CfgInfo& c = kCfgs[cfg];
     const int64_t wgs = tiles_of(cfg, M, n_cols) * batch;
     if (wgs_out) *wgs_out = wgs;
-    const int64_t rounds = (wgs + kNumCUs - 1) / kNumCUs;
+    const int64_t rounds = (wgs + slots_of(cfg) - 1) / slots_of(cfg);
     const int64_t nch = (K + 127) / 128;
     const int64_t per = ((nch + c.ks - 1) / c.ks + 3) / 4 * 4;
-    return (double)rounds * (double)per * (c.wave_cols * c.nw / 4 / 128.0) * (c.bm / 128.0) *
-           (c.ks > 1 ? 1.1 : 1.0) * (c.nw == 8 ? 0.85 : 1.0) * (c.bm < 128 ? 1.6 : 1.0);
+    const int waves_per_simd = c.nw * c.occ / 4;
+    return (double)rounds * (kRoundLatency + (double)per * (c.wave_cols * waves_per_simd / 128.0) * (c.bm / 128.0) *
+                                                 (c.ks > 1 ? 1.1 : 1.0) * (waves_per_simd == 2 ? 0.85 : 1.0) *
+                                                 (c.bm < 128 ? 1.6 : 1.0));
 }
+
+// Column counts [0, n) that configuration cfg can take in whole tiles, leaving the
+// rest to a narrower configuration: every whole tile, or the widest part that fills
+// whole rounds of resident workgroups (so that a few main tiles do not spill into a
+// round of their own).  Returns how many of the two exist.
+int main_splits(int cfg, int64_t M, int64_t N, int64_t batch, int64_t (&n)[2]) {
+    const int64_t bn = kCfgs[cfg].bn;
+    const int64_t whole = N / bn * bn;
+    int cnt = 0;
+    if (whole > 0 && whole < N) n[cnt++] = whole;
+    const int64_t tiles_m = (M + kCfgs[cfg].bm - 1) / kCfgs[cfg].bm * batch;
+    const int64_t per_round = slots_of(cfg) / tiles_m;  // column tiles per round
+    if (per_round >= 1) {
+        const int64_t fill = N / bn / per_round * per_round * bn;
+        if (fill > 0 && fill < N && (cnt == 0 || fill != n[0])) n[cnt++] = fill;
+    }
+    return cnt;
+}
+
+// Modelled time of main configuration mc over [0, n_main) plus tc over the rest, in
+// one launch: the tail's workgroups take the slots the main part leaves free, then the
+// ones that free up first.  With two groups per CU a tail group runs beside a main
+// group that is still busy, which hides about half of its cost (measured).
+double split_cost(int mc, int tc, int64_t n_main, int64_t M, int64_t N, int64_t K, int64_t batch) {
+    int64_t wm = 0, wt = 0;
+    const double cm = part_cost(mc, M, n_main, K, batch, &wm);
+    const double ct = part_cost(tc, M, N - n_main, K, batch, &wt) * (kCfgs[mc].occ > 1 ? 0.5 : 1.0);
+    const int64_t free_slots = (slots_of(mc) - wm % slots_of(mc)) % slots_of(mc);
+    return wt <= free_slots ? (cm > ct ? cm : ct) : cm + ct;
+}
+
+bool tail_fits(int mc, int tc) { return tc >= 0 && (kTails[mc][0] == tc || kTails[mc][1] == tc); }
 
 Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t batch, int force, int force_tail) {
     if (force >= 0 && force < kNumCfgs) {
-        // pinned: whole tiles of `force`, the rest (if any) on `force_tail` when that
-        // is a narrower configuration
-        const int64_t n_main = N / kCfgs[force].bn * kCfgs[force].bn;
-        if (force_tail >= 0 && force_tail < kNumCfgs && kCfgs[force_tail].bn < kCfgs[force].bn &&
-            kCfgs[force_tail].nw == kCfgs[force].nw && n_main > 0 && n_main < N)
-            return Plan{force, force_tail, (int)n_main};
-        return Plan{force, -1, (int)N};
+        // pinned: `force`, with the columns past its main part (the cheaper of its
+        // splits) on `force_tail` when `force` has an instance with that tail
+        int64_t n[2];
+        const int cnt = force_tail < kNumCfgs && tail_fits(force, force_tail)
+                            ? main_splits(force, M, N, batch, n)
+                            : 0;
+        if (cnt == 0) return Plan{force, -1, (int)N};
+        int64_t pick = n[0];
+        if (cnt == 2 && split_cost(force, force_tail, n[1], M, N, K, batch) <
+                            split_cost(force, force_tail, n[0], M, N, K, batch))
+            pick = n[1];
+        return Plan{force, force_tail, (int)pick};
     }
     Plan best{0, -1, (int)N};
     double best_cost = 1e300;
     for (int mc = 0; mc < kNumCfgs; ++mc) {
-        int64_t wgs_main = 0;
-        const double whole = part_cost(mc, M, N, K, batch, &wgs_main);
+        const double whole = part_cost(mc, M, N, K, batch, nullptr);
         if (whole < best_cost) {
             best_cost = whole;
             best = Plan{mc, -1, (int)N};
         }
-        // whole main tiles, the remainder on a narrower configuration in the same
-        // launch: its workgroups take the CUs the main part leaves free, then the CUs
-        // that finish first
-        const int64_t n_main = N / kCfgs[mc].bn * kCfgs[mc].bn;
-        if (n_main == 0 || n_main == N) continue;
-        for (int tc = 0; tc < kNumCfgs; ++tc) {
-            if (kCfgs[tc].bn >= kCfgs[mc].bn || kCfgs[tc].nw != kCfgs[mc].nw) continue;
-            int64_t wm = 0, wt = 0;
-            const double cm = part_cost(mc, M, n_main, K, batch, &wm);
-            const double ct = part_cost(tc, M, N - n_main, K, batch, &wt);
-            const int64_t free_cus = (kNumCUs - wm % kNumCUs) % kNumCUs;
-            const double cost = wt <= free_cus ? (cm > ct ? cm : ct) : cm + ct;
-            if (cost < best_cost) {
-                best_cost = cost;
-                best = Plan{mc, tc, (int)n_main};
+        int64_t n[2];
+        const int cnt = main_splits(mc, M, N, batch, n);
+        for (int s = 0; s < cnt; ++s) {
+            for (int tc = 0; tc < kNumCfgs; ++tc) {
+                if (!tail_fits(mc, tc)) continue;
+                const double cost = split_cost(mc, tc, n[s], M, N, K, batch);
+                if (cost < best_cost) {
+                    best_cost = cost;
+                    best = Plan{mc, tc, (int)n[s]};
+                }
             }
         }
     }
@@ -630,17 +678,17 @@ Seg make_seg(int64_t M, int n_begin, int n_end) {
     return Seg{(int)((M + C::BM - 1) / C::BM), (n_end - n_begin + C::BN - 1) / C::BN, n_begin, n_end};
 }
 
+// T0 and T1 are the configurations kTails lists for C0 (a repeat where it has fewer).
 template <class C0, class T0, class T1>
-hipError_t launch_main(const prefill::Args& a, const Plan& p, int tail0, int tail1, int64_t batch,
-                       hipStream_t stream) {
+hipError_t launch_main(const prefill::Args& a, const Plan& p, int64_t batch, hipStream_t stream) {
     const Seg s0 = make_seg<C0>(a.M, 0, p.n_split);
     const Seg none{0, 0, a.N, a.N};
-    if (p.tail_cfg >= 0 && p.tail_cfg == tail0)
+    const int* const tails = kTails[p.main_cfg];
+    if (p.tail_cfg >= 0 && p.tail_cfg == tails[0])
         return launch2<C0, T0>(a, s0, make_seg<T0>(a.M, p.n_split, a.N), batch, stream);
-    if (p.tail_cfg >= 0 && p.tail_cfg == tail1)
+    if (p.tail_cfg >= 0 && p.tail_cfg == tails[1])
         return launch2<C0, T1>(a, s0, make_seg<T1>(a.M, p.n_split, a.N), batch, stream);
-    // no tail, or a pinned one this main configuration has no instance for: every
-    // column on the main configuration
+    // no tail: every column on the main configuration
     return launch2<C0, C0>(a, make_seg<C0>(a.M, 0, a.N), none, batch, stream);
 }
 
@@ -665,13 +713,15 @@ hipError_t launch_gemm_prefill(const int8_t* x_q, const float* s_x, int64_t M, i
     const prefill::Args a{x_q, s_x, w_bits, s_w, w_a, s_a, s_b, t, y, acc_dbg, (int)M, (int)N, (int)K, rank};
     const Plan p = plan_for(M, N, K, batch, force_cfg, force_tail);
     switch (p.main_cfg) {
-        case 0: return launch_main<C441, C422, C412>(a, p, 1, 2, batch, stream);
-        case 1: return launch_main<C422, C412, C412>(a, p, 2, 2, batch, stream);
-        case 2: return launch_main<C412, C412, C412>(a, p, -1, -1, batch, stream);
-        case 3: return launch_main<C4218, C2128, C2148>(a, p, 5, 6, batch, stream);
-        case 4: return launch_main<C4128, C2128, C2148>(a, p, 5, 6, batch, stream);
-        case 5: return launch_main<C2128, C2148, C2148>(a, p, 6, 6, batch, stream);
-        default: return launch_main<C2148, C2148, C2148>(a, p, -1, -1, batch, stream);
+        case 0: return launch_main<C441, C422, C412>(a, p, batch, stream);
+        case 1: return launch_main<C422, C412, C412>(a, p, batch, stream);
+        case 2: return launch_main<C412, C412, C412>(a, p, batch, stream);
+        case 3: return launch_main<C4218, C2128, C2148>(a, p, batch, stream);
+        case 4: return launch_main<C4128, C2128, C2148>(a, p, batch, stream);
+        case 5: return launch_main<C2128, C2148, C2148>(a, p, batch, stream);
+        case 6: return launch_main<C2148, C2148, C2148>(a, p, batch, stream);
+        case 7: return launch_main<C4214, C2124, C2124>(a, p, batch, stream);
+        default: return launch_main<C2124, C2124, C2124>(a, p, batch, stream);
     }
 }
 

@@ -14,7 +14,7 @@ from test_gpu_parity import _check_full, torch_cuda  # noqa: F401  (fixture)
 
 pytestmark = pytest.mark.gpu
 
-N_CFGS = 7                      # tile configurations of the prefill kernel
+N_CFGS = 9                      # tile configurations of the prefill kernel
 CFGS = list(range(N_CFGS)) + [-2]
 
 SHAPES = [
@@ -34,7 +34,8 @@ def test_prefill_config_parity(torch_cuda, monkeypatch, cfg, M, N, K):
     _check_full(si.make_problem(M, N, K, max(1, K // 100), seed=M * 31 + N * 7 + K + 5 * cfg))
 
 
-@pytest.mark.parametrize("main,tail", [(0, 1), (0, 2), (1, 2), (3, 5), (3, 6), (4, 5), (4, 6), (5, 6), (3, 4)])
+@pytest.mark.parametrize("main,tail", [(0, 1), (0, 2), (1, 2), (3, 5), (3, 6), (4, 5), (4, 6), (5, 6), (7, 8),
+                                       (3, 4)])
 @pytest.mark.parametrize("M,N,K", [(130, 700, 1024), (64, 1000, 256), (2048, 8512, 512)])
 def test_prefill_main_plus_tail(torch_cuda, monkeypatch, main, tail, M, N, K):
     # whole tiles of one configuration and the remaining columns on a narrower one,
