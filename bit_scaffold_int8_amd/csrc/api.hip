@@ -133,7 +133,8 @@ dfssm_status gemm_impl(const int8_t* x_q, const float* s_x, int64_t M, int64_t N
         // DFSSM_PREFILL_CFG pins the many-token kernel's tile configuration (0 ..
         // prefill_num_cfgs() - 1) or, with -2, the generic fallback kernel; unset or -1
         // lets the cost model choose.  DFSSM_PREFILL_TAIL adds a narrower configuration
-        // for the columns past the pinned one's last whole tile.  Testing and tuning knobs.
+        // for the columns past the pinned one's main part, where the pinned one is built
+        // with that tail.  Testing and tuning knobs.
         int force = -1, force_tail = -1;
         if (const char* f = getenv("DFSSM_PREFILL_CFG")) force = atoi(f);
         if (const char* f = getenv("DFSSM_PREFILL_TAIL")) force_tail = atoi(f);

@@ -131,7 +131,9 @@ dfssm_status dfssm_quantize_lora_down_strided_batched(const float* x, int64_t M,
  * fallback kernel); either way one kernel launch.  For tests and tuning, the
  * environment variable DFSSM_PREFILL_CFG pins the MFMA kernel's tile configuration
  * (0, 1, ...; -2 = the generic kernel) and DFSSM_PREFILL_TAIL a narrower one for the
- * columns past the pinned one's last whole tile; results are the same either way.
+ * columns past the pinned one's main part, where the pinned configuration is built
+ * with that tail (otherwise every column runs on the pinned one); results are the
+ * same either way.
  */
 dfssm_status dfssm_scaffold_lora_gemm(const int8_t* x_q, const float* s_x,
                                       int64_t M, int64_t N, int64_t K,
