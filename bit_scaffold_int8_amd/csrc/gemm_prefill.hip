@@ -573,8 +573,9 @@ int64_t slots_of(int cfg) { return (int64_t)kNumCUs * kCfgs[cfg].occ; }
 // launch: ~2.3 units, fitted to the measured cost of a short second round) plus the
 // steps of one SIMD (a chunk count rounded up to the 4-chunk sign block; the SIMD
 // serves one wave of each co-resident group), 10 % extra for the split-K hand-over,
-// 15 % less with two waves per SIMD (measured: their stalls overlap), and 60 % more
-// for 64-row tiles (half the MFMAs per expanded sign operand).
+// 15 % less with two waves per SIMD (measured: their stalls overlap), 1 % more with
+// two groups per CU (measured on one round of 128 x 256 tiles against 128 x 512), and
+// 60 % more for 64-row tiles (half the MFMAs per expanded sign operand).
 constexpr double kRoundLatency = 2.3;
 double part_cost(int cfg, int64_t M, int64_t n_cols, int64_t K, int64_t batch, int64_t* wgs_out) {
     const CfgInfo& c = kCfgs[cfg];
@@ -586,7 +587,7 @@ double part_cost(int cfg, int64_t M, int64_t n_cols, int64_t K, int64_t batch, i
     const int waves_per_simd = c.nw * c.occ / 4;
     return (double)rounds * (kRoundLatency + (double)per * (c.wave_cols * waves_per_simd / 128.0) * (c.bm / 128.0) *
                                                  (c.ks > 1 ? 1.1 : 1.0) * (waves_per_simd == 2 ? 0.85 : 1.0) *
-                                                 (c.bm < 128 ? 1.6 : 1.0));
+                                                 (c.occ > 1 ? 1.01 : 1.0) * (c.bm < 128 ? 1.6 : 1.0));
 }
 
 // Column counts [0, n) that configuration cfg can take in whole tiles, leaving the
@@ -609,12 +610,14 @@ int main_splits(int cfg, int64_t M, int64_t N, int64_t batch, int64_t (&n)[2]) {
 
 // Modelled time of main configuration mc over [0, n_main) plus tc over the rest, in
 // one launch: the tail's workgroups take the slots the main part leaves free, then the
-// ones that free up first.  With two groups per CU a tail group runs beside a main
-// group that is still busy, which hides about half of its cost (measured).
+// ones that free up first.  With two groups per CU and a main part of one round, a
+// tail group runs beside a main group that is still busy, which hides about half of
+// its cost (measured; behind two or more main rounds it hid nothing measurable).
 double split_cost(int mc, int tc, int64_t n_main, int64_t M, int64_t N, int64_t K, int64_t batch) {
     int64_t wm = 0, wt = 0;
     const double cm = part_cost(mc, M, n_main, K, batch, &wm);
-    const double ct = part_cost(tc, M, N - n_main, K, batch, &wt) * (kCfgs[mc].occ > 1 ? 0.5 : 1.0);
+    const bool beside = kCfgs[mc].occ > 1 && wm <= slots_of(mc);
+    const double ct = part_cost(tc, M, N - n_main, K, batch, &wt) * (beside ? 0.5 : 1.0);
     const int64_t free_slots = (slots_of(mc) - wm % slots_of(mc)) % slots_of(mc);
     return wt <= free_slots ? (cm > ct ? cm : ct) : cm + ct;
 }
