@@ -138,6 +138,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the per-call graph and prefill legs")
+    ap.add_argument("--no-sweeps", action="store_true",
+                    help="skip the launch-heavy legs (per-call graphs, 48-layer sweep and chain) and the "
+                         "cooperative barrier probe: counter runs, where every dispatch is serialized")
     ap.add_argument("--prefill-iters", type=int, default=10)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMV traffic record from two rocprofv3 counter_collection.csv files")
@@ -146,6 +149,11 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="run the empty-kernel and copy probes even with --no-extras (counter calibration)")
     return ap.parse_args()
+
+
+def progress(leg):
+    """One line on stderr per finished leg (stdout carries only the JSON line)."""
+    print(f"bench: {leg} done", file=sys.stderr, flush=True)
 
 
 def time_events(torch, fn, iters, stream):
@@ -578,7 +586,7 @@ def main():
         },
     }
 
-    if not args.no_extras:
+    if not args.no_extras and not args.no_sweeps:
         # per-call latency: every copy's two launches captured in one hipGraph
         single = [DeviceProjections(
             x=dp.x[b:b + 1], w_bits=dp.w_bits[b:b + 1], s_w=dp.s_w[b:b + 1], w_a=dp.w_a[b:b + 1],
@@ -607,7 +615,9 @@ def main():
             del g
         per_call["note"] = "R rotated single-problem calls captured in one hipGraph"
         out["per_call_graph"] = per_call
+        progress("per-call graphs")
 
+    if not args.no_extras:
         # prefill: M=2048 tokens on the int8 MFMA path
         pre = {}
         for name, (pM, pN, pK, po) in zip(("in_proj", "out_proj"), si.CONFIGS["prefill_m2048"]["shapes"]):
@@ -622,6 +632,7 @@ def main():
                          "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
             del pp
         out["prefill_m2048"] = pre
+        progress("prefill")
         # what the matrix cores sustain on this kind of data, for the prefill TOPS above
         probe = mfma_probe()
         out["mfma_i8_probe"] = probe
@@ -642,12 +653,20 @@ def main():
             "gemv_GBps": round(64 * gemm_call_bytes(M, N, K) / (g64 * 1e-3) / 1e9, 1),
             "note": "warm: 64 copies fit the 256 MB Infinity Cache"}
         out["in_proj_decode_k2048_n8512"] = in_proj_decode(torch, dev, stream, args.steps, args.warmup)
-        out["decode_sweep_48l"] = decode_sweep_48l(torch, dev, 128)   # 128 tokens back to back
+        progress("in_proj decode")
+        if not args.no_sweeps:
+            out["decode_sweep_48l"] = decode_sweep_48l(torch, dev, 128)   # 128 tokens back to back
+            progress("48-layer sweep")
         out["mamba2_decode_step"] = mamba2_step_bench(torch, dev, 20)
-        out["decode_chain_48l"] = decode_chain_48l(torch, dev, 64)    # 64 two-token replays
+        progress("Mamba-2 step")
+        if not args.no_sweeps:
+            out["decode_chain_48l"] = decode_chain_48l(torch, dev, 64)    # 64 two-token replays
+            progress("48-layer chain")
         out["lm_head_decode_v50280_d2048"] = lm_head_decode(torch, dev, stream, args.steps, args.warmup)
+        progress("LM head")
         out["probes"] = probes(torch, stream)
-        out["grid_barrier_probe"] = barrier_probe()
+        if not args.no_sweeps:
+            out["grid_barrier_probe"] = barrier_probe()
 
     if args.no_extras and args.copy_probe:
         out["probes"] = probes(torch, stream)
