@@ -40,6 +40,8 @@ hipError_t launch_mamba2_step(const float* zxbcdt, int64_t S, int nheads, const 
                               hipStream_t stream);
 bool prefill_supported(int64_t M, int64_t N, int64_t K);
 int prefill_num_cfgs();
+void prefill_plan_query(int64_t M, int64_t N, int64_t K, int64_t batch, int* main_cfg, int* tail_cfg,
+                        int64_t* n_split);
 hipError_t launch_gemm_prefill(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                                const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
                                const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
@@ -214,6 +216,27 @@ const char* dfssm_status_string(dfssm_status status) {
 }
 
 int32_t dfssm_version(void) { return 300; }
+
+dfssm_status dfssm_prefill_plan(int64_t M, int64_t N, int64_t K, int64_t batch, int32_t* main_cfg,
+                                int32_t* tail_cfg, int64_t* n_split) {
+    if (!main_cfg || !tail_cfg || !n_split) return DFSSM_ERR_INVALID_ARG;
+    if (dfssm_status st = check_sizes(M, K, batch)) return st;
+    if (N <= 0 || N >= kMaxRows || (K % 8) != 0) return DFSSM_ERR_INVALID_ARG;
+    if (K > kMaxK) return DFSSM_ERR_UNSUPPORTED;
+    // the same tests as dfssm_scaffold_lora_gemm[_strided_batched]: the decode kernel, or
+    // the generic kernel, takes the shape
+    const bool gemv_fits = N * (K / 8) < ((int64_t)1 << 31) && M * N * 4 < ((int64_t)1 << 31) &&
+                           N * kRankBytes < ((int64_t)1 << 31);
+    if (M <= kMaxDecodeM && K <= kGemvMaxK && gemv_fits) return DFSSM_ERR_UNSUPPORTED;
+    if (!dfssm::prefill_supported(M, N, K)) return DFSSM_ERR_UNSUPPORTED;
+    int mc = 0, tc = -1;
+    int64_t ns = N;
+    dfssm::prefill_plan_query(M, N, K, batch, &mc, &tc, &ns);
+    *main_cfg = mc;
+    *tail_cfg = tc;
+    *n_split = ns;
+    return DFSSM_OK;
+}
 
 dfssm_status dfssm_quantize_act(const float* x, int64_t M, int64_t K, int8_t* x_q, float* s_x,
                                 hipStream_t stream) {

@@ -697,6 +697,16 @@ hipError_t launch_main(const prefill::Args& a, const Plan& p, int64_t batch, hip
 
 }  // namespace
 
+// The cost model's plan for a shape (host only, no launch): the main configuration, the
+// tail configuration (-1: none) and the first column of the tail.
+void prefill_plan_query(int64_t M, int64_t N, int64_t K, int64_t batch, int* main_cfg, int* tail_cfg,
+                        int64_t* n_split) {
+    const Plan p = plan_for(M, N, K, batch, -1, -1);
+    *main_cfg = p.main_cfg;
+    *tail_cfg = p.tail_cfg;
+    *n_split = p.tail_cfg >= 0 ? p.n_split : N;
+}
+
 // Tile configurations the prefill kernel can be pinned to by tests (index; -1 = pick
 // by the cost model; a tail configuration applies to the columns past the last whole
 // main tile).

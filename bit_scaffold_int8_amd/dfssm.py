@@ -23,7 +23,8 @@ EXPORTED = ("dfssm_status_string", "dfssm_version", "dfssm_quantize_act", "dfssm
             "dfssm_quantize_lora_down_strided_batched", "dfssm_scaffold_lora_gemm",
             "dfssm_scaffold_lora_gemm_strided_batched", "dfssm_scaffold_lora_forward",
             "dfssm_scaffold_lora_forward_strided_batched", "dfssm_int8_rowscale_gemm",
-            "dfssm_int8_rowscale_gemm_strided_batched", "dfssm_embedding_lookup", "dfssm_mamba2_decode_step")
+            "dfssm_int8_rowscale_gemm_strided_batched", "dfssm_embedding_lookup", "dfssm_mamba2_decode_step",
+            "dfssm_prefill_plan")
 
 
 class DfssmError(RuntimeError):
@@ -56,6 +57,7 @@ def _load():
         "dfssm_int8_rowscale_gemm_strided_batched": [P, P, i64, i64, i64, P, P, P, P, i64, P],
         "dfssm_embedding_lookup": [P, i64, P, P, i64, i64, P, P],
         "dfssm_mamba2_decode_step": [P, i64, i64, i64, i64, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P],
+        "dfssm_prefill_plan": [i64, i64, i64, i64, P, P, P],
     }
     for name, argtypes in sigs.items():
         f = getattr(lib, name)
@@ -73,6 +75,14 @@ def status_string(status: int) -> str:
 
 def dfssm_version() -> int:
     return int(lib.dfssm_version())
+
+
+def dfssm_prefill_plan(M: int, N: int, K: int, batch: int = 1):
+    """(main configuration, tail configuration or -1, first tail column) the MFMA
+    kernel's cost model picks for this shape; host only."""
+    mc, tc, ns = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int64(0)
+    _call("dfssm_prefill_plan", M, N, K, batch, ctypes.addressof(mc), ctypes.addressof(tc), ctypes.addressof(ns))
+    return mc.value, tc.value, ns.value
 
 
 def _ptr(t):

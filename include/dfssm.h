@@ -80,6 +80,22 @@ const char* dfssm_status_string(dfssm_status status);
 /* Library version as major*100 + minor. */
 int32_t dfssm_version(void);
 
+/* The tile plan the int8 MFMA kernel takes for a dfssm_scaffold_lora_gemm[_strided_batched]
+ * call of this shape, as its cost model picks it (the DFSSM_PREFILL_CFG / _TAIL pins are
+ * not applied).  Host only: launches nothing and needs no GPU.  A testing and tuning
+ * aid.  Outputs (host pointers, written on DFSSM_OK):
+ *   main_cfg  the configuration of columns [0, n_split) (0, 1, ...)
+ *   tail_cfg  the configuration of columns [n_split, N), or -1 (then n_split = N)
+ * Configurations: 0 128x512 (4 waves), 1 128x128 split-K 2, 2 128x64 split-K 2,
+ * 3 128x512 (8 waves), 4 128x128 split-K 2 (8 waves), 5 64x128 split-K 2 (8 waves),
+ * 6 64x64 split-K 4 (8 waves), 7 128x256 (4 waves, two groups per CU), 8 64x64
+ * split-K 2 (4 waves, two groups per CU).
+ * Returns DFSSM_ERR_INVALID_ARG for NULL outputs or sizes the call would reject, and
+ * DFSSM_ERR_UNSUPPORTED when the call would take another kernel: the decode kernel
+ * (M <= 16) or the generic one (K % 64 != 0), or K > 131072. */
+dfssm_status dfssm_prefill_plan(int64_t M, int64_t N, int64_t K, int64_t batch, int32_t* main_cfg,
+                                int32_t* tail_cfg, int64_t* n_split);
+
 /*
  * Per-token absmax int8 quantization of activations, the int8 operand of the
  * scaffold product (technical summary section 2C).

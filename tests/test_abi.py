@@ -200,3 +200,51 @@ def _mamba2(**kw):
 ])
 def test_mamba2_step_rejects(kw, want):
     assert _mamba2(**kw) == want
+
+
+# ---- the prefill planner (host only)
+
+def test_prefill_plan_keeps_the_measured_choices():
+    from bit_scaffold_int8_amd import dfssm
+    # plans chosen by timing them against each other on an MI355X: in_proj M2048 on
+    # 128x256 tiles at two groups per CU with a 64x64 split-K tail (43.4 us against 46.5
+    # for one 8-wave group per CU plus a tail round); out_proj on 128x128 split-K; at
+    # M4096 and at batch 4 one 8-wave group per CU with a 64x128 split-K tail (88.2 and
+    # 187.0 us, against 93.3 and 189.6 for two groups per CU)
+    assert dfssm.dfssm_prefill_plan(2048, 8512, 2048) == (7, 8, 8192)
+    assert dfssm.dfssm_prefill_plan(2048, 2048, 4096) == (4, -1, 2048)
+    assert dfssm.dfssm_prefill_plan(4096, 8512, 2048) == (3, 5, 8192)
+    assert dfssm.dfssm_prefill_plan(2048, 8512, 2048, 4) == (3, 5, 8192)
+
+
+# column width of each configuration and the tails it is built with (the header's list)
+_PF_BN = {0: 512, 1: 128, 2: 64, 3: 512, 4: 128, 5: 128, 6: 64, 7: 256, 8: 64}
+_PF_TAILS = {0: (1, 2), 1: (2,), 2: (), 3: (5, 6), 4: (5, 6), 5: (6,), 6: (), 7: (8,), 8: ()}
+
+
+@pytest.mark.parametrize("M", [17, 100, 128, 300, 512, 2048, 4096])
+@pytest.mark.parametrize("N,K", [(1, 64), (70, 192), (513, 1024), (2048, 4096), (8512, 2048), (8704, 2048)])
+@pytest.mark.parametrize("batch", [1, 3])
+def test_prefill_plan_is_consistent(M, N, K, batch):
+    from bit_scaffold_int8_amd import dfssm
+    mc, tc, ns = dfssm.dfssm_prefill_plan(M, N, K, batch)
+    assert mc in _PF_BN
+    if tc < 0:
+        assert ns == N
+    else:
+        assert tc in _PF_TAILS[mc]              # a tail the main configuration is built with
+        assert 0 < ns < N and ns % _PF_BN[mc] == 0
+        assert _PF_BN[tc] < _PF_BN[mc]
+
+
+def test_prefill_plan_rejects():
+    from bit_scaffold_int8_amd import dfssm
+    U, I = dfssm.DFSSM_ERR_UNSUPPORTED, dfssm.DFSSM_ERR_INVALID_ARG
+    for args, want in [((16, 512, 2048, 1), U),      # the decode kernel's shape
+                       ((2048, 512, 808, 1), U),     # K % 64 != 0: the generic kernel
+                       ((2048, 512, 804, 1), I),     # K % 8 != 0
+                       ((0, 512, 2048, 1), I), ((2048, 0, 2048, 1), I), ((2048, 512, 2048, 0), I)]:
+        with pytest.raises(dfssm.DfssmError) as e:
+            dfssm.dfssm_prefill_plan(*args)
+        assert e.value.status == want, args
+    assert dfssm.lib.dfssm_prefill_plan(2048, 512, 2048, 1, None, None, None) == I
