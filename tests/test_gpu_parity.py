@@ -123,9 +123,16 @@ def test_prefill_m2048_sampled(torch_cuda, which):
     assert np.array_equal(got["x_q"], xq_ref)
     assert np.array_equal(got["t"], oracle.lora_down(xq_ref, prob.W_B))
     srng = np.random.default_rng(99)
-    # random positions plus every tile corner and the ragged edges
+    # random positions plus every tile corner and the ragged edges, and the seams of the
+    # plans the cost model picks: 64-, 128- and 256-column tiles, 64- and 128-row tiles,
+    # and the first column of a narrow tail (8192 of 8512)
     mi = np.concatenate([srng.integers(0, prob.M, 3000), [0, prob.M - 1, 127, 128, 0, prob.M - 1]])
     ni = np.concatenate([srng.integers(0, prob.N, 3000), [0, prob.N - 1, 0, prob.N - 1, 127, 128]])
+    seam_cols = [c for c in (63, 64, 255, 256, 511, 512, 8191, 8192, 8193, prob.N - 65, prob.N - 64)
+                 if 0 <= c < prob.N]
+    seam_rows = [63, 64, 127, 128, 1023, 1024, prob.M - 65, prob.M - 64]
+    mi = np.concatenate([mi, np.repeat(seam_rows, len(seam_cols))])
+    ni = np.concatenate([ni, np.tile(seam_cols, len(seam_rows))])
     y_ref, acc_ref, t_ref = oracle.scaffold_lora_at(xq_ref, sx_ref, prob.P, prob.s_w, prob.W_A, prob.s_A,
                                                     prob.W_B, prob.s_B, mi, ni)
     assert np.array_equal(got["acc"][mi, ni], acc_ref)
