@@ -1,4 +1,5 @@
-"""The entry points inside captured HIP graphs, replayed several times.
+"""The entry points inside captured HIP graphs, replayed several times, and on two
+streams at once.
 
 The library's calls are asynchronous on the caller's stream and allocate nothing, so
 a caller can capture them; decode runs them that way (the whole per-token sequence in
@@ -122,3 +123,32 @@ def test_mamba2_step_graph_replays_match_eager(torch_cuda):
         assert torch.equal(graph_side.windows[0].view(torch.int32), eager_side.windows[0].view(torch.int32)), \
             f"replay {r}: window"
         assert torch.equal(graph_side.out.view(torch.int32), eager_side.out.view(torch.int32)), f"replay {r}: out"
+
+
+def test_calls_on_two_streams_at_once_match_sequential(torch_cuda):
+    # the library keeps no per-call state on the device: calls on two streams (default
+    # priority) may run at the same time, each on its own buffers, and give what the
+    # same calls give one after another
+    import torch
+    from bit_scaffold_int8_amd.runner import DeviceProjections
+    a = DeviceProjections.from_problems([si.make_problem(1, 2048, 4096, 2, seed=500 + b) for b in range(4)],
+                                        device="cuda")
+    b = DeviceProjections.from_problems([si.make_problem(2, 8512, 2048, 2, seed=600 + j) for j in range(2)],
+                                        device="cuda")
+    c = DeviceProjections.from_problems([si.make_problem(200, 700, 1024, 3, seed=700)], device="cuda")
+    for p in (a, b, c):
+        p.forward_one_call(debug=False)
+    torch.cuda.synchronize()
+    want = [p.y.clone() for p in (a, b, c)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for r in range(3):
+        for p in (a, b, c):
+            p.y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        for _ in range(2):   # interleaved launches on both streams
+            a.forward_one_call(s1, debug=False)
+            b.forward_one_call(s2, debug=False)
+            c.forward(s1, debug=False)
+        torch.cuda.synchronize()
+        for name, p, w in zip("abc", (a, b, c), want):
+            assert torch.equal(p.y.view(torch.int32), w.view(torch.int32)), f"round {r}: {name} differs"
