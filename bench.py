@@ -129,18 +129,38 @@ def traffic_from(fetch_csv, write_csv, cmd):
     print(json.dumps(rec))
 
 
+PROFILE_FILE = os.path.join(ROOT, "profiles", "kernel_trace_gemv_kernel_out_proj_decode_512_copies.json")
+
+
+def profiled_launch():
+    """Average and median duration of the headline kernel in the committed rocprofv3
+    kernel trace of the default bench, while the kernel's sources still hash to what
+    was profiled (else None)."""
+    try:
+        with open(PROFILE_FILE) as fh:
+            rec = json.load(fh)
+    except OSError:
+        return None
+    if rec.get("sources_sha256") != sources_sha256(rec.get("sources", GEMV_SOURCES)):
+        return None
+    return {k: rec[k] for k in ("avg_us", "median_us", "launches", "command") if k in rec}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="run the step back to back this long before the warmup steps, so the clocks have "
+                         "settled when the timed region starts")
     ap.add_argument("--copies", type=int, default=512)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the per-call graph and prefill legs")
     ap.add_argument("--no-sweeps", action="store_true",
-                    help="skip the launch-heavy legs (per-call graphs, 48-layer sweep and chain) and the "
-                         "cooperative barrier probe: counter runs, where every dispatch is serialized")
+                    help="skip the launch-heavy legs (per-call graphs, 48-layer sweep and chain): counter "
+                         "runs, where every dispatch is serialized")
     ap.add_argument("--prefill-iters", type=int, default=10)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMV traffic record from two rocprofv3 counter_collection.csv files")
@@ -418,27 +438,6 @@ def mfma_probe():
     return out
 
 
-def barrier_probe():
-    """Microseconds per device-wide barrier round (libdfssm_probe.so): the cost a
-    persistent multi-layer decode kernel would pay between dependent projections."""
-    import ctypes
-    lib = ctypes.CDLL(os.path.join(ROOT, "bit_scaffold_int8_amd", "libdfssm_probe.so"))
-    lib.dfssm_probe_grid_barrier_us.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
-    lib.dfssm_probe_grid_barrier_us.restype = ctypes.c_int
-    out = {}
-    for groups in (256, 512):
-        for fenced in (0, 1):
-            v = ctypes.c_double(0.0)
-            rc = lib.dfssm_probe_grid_barrier_us(groups, fenced, ctypes.byref(v))
-            if rc != 0:
-                raise RuntimeError(f"barrier probe (groups {groups}, fenced {fenced}) failed: {rc}")
-            out[f"g{groups}_{'fenced' if fenced else 'coherent_ops'}_us"] = round(v.value, 2)
-    out["note"] = ("cooperative launch of 512-thread groups; per round: 64 floats written per group, a "
-                   "hierarchical counter barrier, 2048 floats read back; fenced = agent-scope release/acquire "
-                   "fences, coherent_ops = agent-scope atomic loads/stores of the data, no fences")
-    return out
-
-
 def head_bytes(M, N, K):
     """Algorithmic bytes of one int8 LM-head call given the codes: E, s_e, x_q, s_x, y."""
     return N * K + 4 * N + M * K + 4 * M + 4 * M * N
@@ -551,25 +550,35 @@ def main():
     def step():
         dp.forward_one_call(stream, debug=False)
 
+    # clock settle: the step back to back for a fixed time (the shader and memory clocks
+    # ramp under load; steps timed right after a cold start run ~10 % slow), then the
+    # warmup steps as asked
+    t_settle, settle_steps = time.perf_counter(), 0
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        for _ in range(20):
+            step()
+        settle_steps += 20
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: K whole steps.  A step is one launch of the dominant kernel, so an
+    # event after every step (on the kernel's stream) gives each launch's duration plus
+    # the dispatch gap to the next, from the same region that `value` comes from.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for k in range(args.steps):
         step()
-    end.record(stream)
+        evs[k + 1].record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    total_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = total_ms / args.steps
-
-    # the dominant kernel (the step's one launch over all copies), timed live on its
-    # stream: K back-to-back launches between two events, so the average is the
-    # kernel's duration plus only the dispatch gap between consecutive launches
-    launch_ms = time_events(torch, step, args.steps, stream)
+    per_launch_ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps))
+    median_launch_ms = per_launch_ms[len(per_launch_ms) // 2]
+    launch_ms = ms_per_step  # mean over the timed region: the step is the launch
     # the same step as two calls (quantize + LoRA-down, then the scaffold GEMV)
     two_ms = time_events(torch, lambda: (dp.quantize_lora_down(stream), dp.gemm(stream, debug=False)),
                          args.steps, stream)
@@ -595,7 +604,11 @@ def main():
             "M": M, "K": K, "N": N, "rank": RANK,
             "copies_rotated": R, "rotated_weight_bytes": weight_bytes,
             "launch": "one strided-batched launch per step over all copies (dfssm_scaffold_lora_forward)",
+            "basis": "steady-state streaming: each launch runs the whole projection for 512 independent "
+                     "M=1 problems (cold weights); per-call latency of a single M=1 projection is in "
+                     "per_call_graph",
         },
+        "settle": {"seconds": round(settle_s, 2), "steps": settle_steps},
         "us_per_gemv_step": round(ms_per_step * 1e3 / R, 4),
         "roofline": {
             "bound": "hbm",
@@ -606,8 +619,11 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(),
             "avg_launch_us": round(launch_ms * 1e3, 3),
-            "timing": "HIP events around back-to-back launches on the kernel's stream",
+            "median_launch_us": round(median_launch_ms * 1e3, 3),
+            "timing": "the timed region itself: HIP events on the kernel's stream after every step (one "
+                      "launch each); avg = the region's mean, median over its launches",
             "algorithmic_bytes_per_launch": R * step_bytes(M, N, K),
+            "profile": profiled_launch(),
         },
         "two_call_step": {
             "us_per_step": round(two_ms * 1e3, 2),
@@ -651,16 +667,28 @@ def main():
     if not args.no_extras:
         # prefill: M=2048 tokens on the int8 MFMA path
         pre = {}
-        for name, (pM, pN, pK, po) in zip(("in_proj", "out_proj"), si.CONFIGS["prefill_m2048"]["shapes"]):
-            pp = DeviceProjections.from_problems([si.make_problem(pM, pN, pK, po, seed=4)], device=dev)
+        for name, prob in zip(("in_proj", "out_proj"), si.prefill_problems()):
+            pM, pK, pN = prob.M, prob.K, prob.N
+            pp = DeviceProjections.from_problems([prob], device=dev)
+            pp.forward_contract(debug=False)
             pp.forward(debug=False)
             torch.cuda.synchronize()
+            # settle, then the specified call (t = W_B x_q inside the product), the
+            # quantizer before it, and the split form (t from quantize_lora_down)
+            time_events(torch, lambda: pp.gemm_computing_t(stream, debug=False), 20, stream)
+            g_ms = time_events(torch, lambda: pp.gemm_computing_t(stream, debug=False), args.prefill_iters, stream)
+            qa_ms = time_events(torch, lambda: pp.quantize(stream), args.prefill_iters, stream)
             q_ms = time_events(torch, lambda: pp.quantize_lora_down(stream), args.prefill_iters, stream)
-            g_ms = time_events(torch, lambda: pp.gemm(stream, debug=False), args.prefill_iters, stream)
+            gt_ms = time_events(torch, lambda: pp.gemm(stream, debug=False), args.prefill_iters, stream)
             tops = gemm_ops(pM, pN, pK) / (g_ms * 1e-3) / 1e12
             pre[name] = {"M": pM, "K": pK, "N": pN, "gemm_us": round(g_ms * 1e3, 2),
-                         "quantize_lora_down_us": round(q_ms * 1e3, 2), "TOPS": round(tops, 1),
-                         "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+                         "quantize_us": round(qa_ms * 1e3, 2), "TOPS": round(tops, 1),
+                         "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+                         "split_form": {"quantize_lora_down_us": round(q_ms * 1e3, 2),
+                                        "gemm_given_t_us": round(gt_ms * 1e3, 2),
+                                        "TOPS": round(gemm_ops(pM, pN, pK) / (gt_ms * 1e-3) / 1e12, 1)},
+                         "note": "gemm = dfssm_scaffold_lora_gemm (t computed in the kernel; ops count the "
+                                 "scaffold and both LoRA products)"}
             del pp
         out["prefill_m2048"] = pre
         progress("prefill")
@@ -696,8 +724,6 @@ def main():
         out["lm_head_decode_v50280_d2048"] = lm_head_decode(torch, dev, stream, args.steps, args.warmup)
         progress("LM head")
         out["probes"] = probes(torch, stream)
-        if not args.no_sweeps:
-            out["grid_barrier_probe"] = barrier_probe()
 
     if args.no_extras and args.copy_probe:
         out["probes"] = probes(torch, stream)

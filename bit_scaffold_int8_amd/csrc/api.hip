@@ -17,12 +17,12 @@ hipError_t launch_lora_down(const int8_t* x_q, int64_t M, int64_t K, const int8_
                             int64_t batch, hipStream_t stream);
 hipError_t launch_gemv(const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
                        const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
-                       const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                       int64_t batch, hipStream_t stream);
+                       const int8_t* w_b, const float* s_b, const int32_t* t, int32_t* t_out, int rank, float* y,
+                       int32_t* acc_dbg, int64_t batch, hipStream_t stream);
 hipError_t launch_gemm_mfma(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                             const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
-                            const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                            int64_t batch, hipStream_t stream);
+                            const int8_t* w_b, const float* s_b, const int32_t* t, int32_t* t_out, int rank,
+                            float* y, int32_t* acc_dbg, int64_t batch, hipStream_t stream);
 bool decode_fused_supported(int64_t M, int64_t K);
 hipError_t launch_decode_fused(const float* x, int M, int64_t N, int64_t K, const uint8_t* w_bits,
                                const float* s_w, const int8_t* w_a, const float* s_a, const int8_t* w_b,
@@ -44,8 +44,9 @@ void prefill_plan_query(int64_t M, int64_t N, int64_t K, int64_t batch, int* mai
                         int64_t* n_split);
 hipError_t launch_gemm_prefill(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                                const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
-                               const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                               int64_t batch, int force_cfg, int force_tail, hipStream_t stream);
+                               const int8_t* w_b, const float* s_b, const int32_t* t, int32_t* t_out, int rank,
+                               float* y, int32_t* acc_dbg, int64_t batch, int force_cfg, int force_tail,
+                               hipStream_t stream);
 }  // namespace dfssm
 
 namespace {
@@ -107,30 +108,42 @@ dfssm_status quantize_lora_down_impl(const float* x, int64_t M, int64_t K, const
     return e == hipSuccess ? DFSSM_OK : DFSSM_ERR_HIP;
 }
 
+// The scaffold product with the scale + LoRA-up epilogue.  Exactly one of t (given,
+// from a LoRA-down call) and w_b (t = W_B x_q computed by the kernel; t_out, when not
+// NULL, receives it) is used at rank 16.
 dfssm_status gemm_impl(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                        const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
-                       const float* s_b, const int32_t* t, int32_t rank, float* y, int32_t* acc_dbg, int64_t batch,
-                       hipStream_t stream) {
+                       const int8_t* w_b, const float* s_b, const int32_t* t, int32_t* t_out, int32_t rank, float* y,
+                       int32_t* acc_dbg, int64_t batch, hipStream_t stream) {
     if (!x_q || !s_x || !w_bits || !s_w || !y) return DFSSM_ERR_INVALID_ARG;
     if (dfssm_status st = check_sizes(M, K, batch)) return st;
     if (N <= 0 || N >= kMaxRows || (K % 8) != 0) return DFSSM_ERR_INVALID_ARG;
     if (!aligned16(x_q) || !aligned4(s_x) || !aligned16(w_bits) || !aligned4(s_w) || !aligned4(y) ||
-        !aligned4_or_null(acc_dbg))
+        !aligned4_or_null(acc_dbg) || !aligned4_or_null(t_out))
         return DFSSM_ERR_INVALID_ARG;
     if (dfssm_status st = check_rank(rank)) return st;
     if (rank == 16) {
-        if (!w_a || !s_a || !s_b || !t) return DFSSM_ERR_INVALID_ARG;
-        if (!aligned16(w_a) || !aligned4(s_a) || !aligned4(s_b) || !aligned4(t)) return DFSSM_ERR_INVALID_ARG;
+        if (!w_a || !s_a || !s_b || (!t && !w_b)) return DFSSM_ERR_INVALID_ARG;
+        if (!aligned16(w_a) || !aligned4(s_a) || !aligned4(s_b)) return DFSSM_ERR_INVALID_ARG;
+        if ((t && !aligned4(t)) || (w_b && !aligned16(w_b))) return DFSSM_ERR_INVALID_ARG;
     }
     if (K > kMaxK) return DFSSM_ERR_UNSUPPORTED;
+    if (rank == 0) {
+        w_b = nullptr;
+        t = nullptr;
+        t_out = nullptr;
+    } else if (t) {
+        w_b = nullptr;  // the given-t form
+        t_out = nullptr;
+    }
     hipError_t e;
     // the decode kernel addresses one problem's signs, LoRA rows and outputs with 32-bit
     // offsets
     const bool gemv_fits = N * (K / 8) < ((int64_t)1 << 31) && M * N * 4 < ((int64_t)1 << 31) &&
                            N * kRankBytes < ((int64_t)1 << 31);
     if (M <= kMaxDecodeM && K <= kGemvMaxK && gemv_fits) {
-        e = dfssm::launch_gemv(x_q, s_x, (int)M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch,
-                               stream);
+        e = dfssm::launch_gemv(x_q, s_x, (int)M, N, K, w_bits, s_w, w_a, s_a, w_b, s_b, t, t_out, rank, y, acc_dbg,
+                               batch, stream);
     } else {
         // DFSSM_PREFILL_CFG pins the many-token kernel's tile configuration (0 ..
         // prefill_num_cfgs() - 1) or, with -2, the generic fallback kernel; unset or -1
@@ -143,11 +156,11 @@ dfssm_status gemm_impl(const int8_t* x_q, const float* s_x, int64_t M, int64_t N
         const bool prefill = force != -2 && dfssm::prefill_supported(M, N, K) && aligned16(w_bits) &&
                              (rank == 0 || aligned16(w_a));
         if (prefill) {
-            e = dfssm::launch_gemm_prefill(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg,
-                                           batch, force, force_tail, stream);
+            e = dfssm::launch_gemm_prefill(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, w_b, s_b, t, t_out, rank, y,
+                                           acc_dbg, batch, force, force_tail, stream);
         } else {
-            e = dfssm::launch_gemm_mfma(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch,
-                                        stream);
+            e = dfssm::launch_gemm_mfma(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, w_b, s_b, t, t_out, rank, y,
+                                        acc_dbg, batch, stream);
         }
     }
     return e == hipSuccess ? DFSSM_OK : DFSSM_ERR_HIP;
@@ -181,7 +194,8 @@ dfssm_status forward_impl(const float* x, int64_t M, int64_t N, int64_t K, const
         // the launch plan has several groups per problem at a throughput batch: two kernels
     }
     if (dfssm_status st = quantize_lora_down_impl(x, M, K, w_b, rank, x_q, s_x, t, batch, stream)) return st;
-    return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, stream);
+    return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, nullptr, s_b, t, nullptr, rank, y, acc_dbg, batch,
+                     stream);
 }
 
 dfssm_status int8_head_impl(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K, const int8_t* e,
@@ -215,7 +229,7 @@ const char* dfssm_status_string(dfssm_status status) {
     return "DFSSM_ERR_UNKNOWN";
 }
 
-int32_t dfssm_version(void) { return 300; }
+int32_t dfssm_version(void) { return 400; }
 
 dfssm_status dfssm_prefill_plan(int64_t M, int64_t N, int64_t K, int64_t batch, int32_t* main_cfg,
                                 int32_t* tail_cfg, int64_t* n_split) {
@@ -269,17 +283,41 @@ dfssm_status dfssm_quantize_lora_down_strided_batched(const float* x, int64_t M,
 
 dfssm_status dfssm_scaffold_lora_gemm(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                                       const uint8_t* w_bits, const float* s_w, const int8_t* w_a,
-                                      const float* s_a, const float* s_b, const int32_t* t, int32_t rank,
-                                      float* y, int32_t* acc_dbg, hipStream_t stream) {
-    return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, 1, stream);
+                                      const float* s_a, const int8_t* w_b, const float* s_b, int32_t rank,
+                                      float* y, int32_t* acc_dbg, int32_t* t_dbg, hipStream_t stream) {
+    if (rank != 0 && !w_b) return DFSSM_ERR_INVALID_ARG;
+    return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, w_b, s_b, nullptr, t_dbg, rank, y, acc_dbg, 1,
+                     stream);
 }
 
 dfssm_status dfssm_scaffold_lora_gemm_strided_batched(const int8_t* x_q, const float* s_x, int64_t M, int64_t N,
                                                       int64_t K, const uint8_t* w_bits, const float* s_w,
-                                                      const int8_t* w_a, const float* s_a, const float* s_b,
-                                                      const int32_t* t, int32_t rank, float* y, int32_t* acc_dbg,
-                                                      int64_t batch, hipStream_t stream) {
-    return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, stream);
+                                                      const int8_t* w_a, const float* s_a, const int8_t* w_b,
+                                                      const float* s_b, int32_t rank, float* y, int32_t* acc_dbg,
+                                                      int32_t* t_dbg, int64_t batch, hipStream_t stream) {
+    if (rank != 0 && !w_b) return DFSSM_ERR_INVALID_ARG;
+    return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, w_b, s_b, nullptr, t_dbg, rank, y, acc_dbg, batch,
+                     stream);
+}
+
+dfssm_status dfssm_scaffold_lora_gemm_given_t(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
+                                              const uint8_t* w_bits, const float* s_w, const int8_t* w_a,
+                                              const float* s_a, const float* s_b, const int32_t* t, int32_t rank,
+                                              float* y, int32_t* acc_dbg, hipStream_t stream) {
+    if (rank != 0 && !t) return DFSSM_ERR_INVALID_ARG;
+    return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, nullptr, s_b, t, nullptr, rank, y, acc_dbg, 1,
+                     stream);
+}
+
+dfssm_status dfssm_scaffold_lora_gemm_given_t_strided_batched(const int8_t* x_q, const float* s_x, int64_t M,
+                                                              int64_t N, int64_t K, const uint8_t* w_bits,
+                                                              const float* s_w, const int8_t* w_a, const float* s_a,
+                                                              const float* s_b, const int32_t* t, int32_t rank,
+                                                              float* y, int32_t* acc_dbg, int64_t batch,
+                                                              hipStream_t stream) {
+    if (rank != 0 && !t) return DFSSM_ERR_INVALID_ARG;
+    return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, nullptr, s_b, t, nullptr, rank, y, acc_dbg, batch,
+                     stream);
 }
 
 dfssm_status dfssm_scaffold_lora_forward(const float* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_bits,

@@ -19,6 +19,9 @@
 //  * 0/1 weights give S = sum_{bit=1} x_q; the +-1 result is exact as acc = 2 S - rowsum.
 //  * Epilogue: y = s_x * (s_w * acc + s_A * sum_r W_A[n][r] * (s_B[r] t[m][r])), with
 //    s_B * t and W_A staged in LDS as fp32.
+//  * kTin: t = W_B x_q is computed here too, one v_mfma_i32_16x16x64_i8 per 16 token
+//    rows per K-step (A = the staged codes, B = the 16 rows of W_B); each wave owns 32
+//    of the tile's rows.
 #include "device_common.h"
 
 namespace dfssm {
@@ -30,17 +33,18 @@ __device__ __forceinline__ uint32_t spread_nibble(uint32_t w, int shift) {
     return (((w >> shift) & 0xFu) * 0x00204081u) & 0x01010101u;
 }
 
-template <bool kFast>
+template <bool kFast, bool kTin>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const int8_t* __restrict__ x_q, const float* __restrict__ s_x, int64_t M, int64_t N, int64_t K,
     const uint8_t* __restrict__ w_bits, const float* __restrict__ s_w,
     const int8_t* __restrict__ w_a, const float* __restrict__ s_a, const float* __restrict__ s_b,
     const int32_t* __restrict__ t, int rank, float* __restrict__ y, int32_t* __restrict__ acc_dbg,
-    int64_t tiles_n) {
+    int64_t tiles_n, const int8_t* __restrict__ w_b, int32_t* __restrict__ t_out) {
     __shared__ __align__(16) uint8_t As[kBM * kLdA];
     __shared__ int32_t rowsum[kBM];
     __shared__ float uS[kBM][kRank + 1];
     __shared__ float waS[kBN][kRank + 1];
+    __shared__ int32_t tS[kTin ? kBM : 1][kRank];
 
     // problem blockIdx.y of a dense batch (every operand advanced by its own size)
     {
@@ -55,7 +59,12 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
             w_a += p * N * kRank;
             s_a += p * N;
             s_b += p * kRank;
-            t += p * M * kRank;
+            if (kTin) {
+                w_b += p * kRank * K;
+                if (t_out) t_out += p * M * kRank;
+            } else {
+                t += p * M * kRank;
+            }
         }
     }
 
@@ -90,6 +99,10 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = (v16i){};
+    // kTin: W_B row (lane & 15), k-slice 16 (lane >> 4) of each K-step; rows
+    // 32 wave + 16 j + (lane & 15) of the tile
+    const uint8_t* wbrow = reinterpret_cast<const uint8_t*>(kTin ? w_b : x_q) + (kTin ? (int64_t)(lane & 15) * K : 0);
+    v4i tacc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 
     for (int64_t k0 = 0; k0 < K; k0 += kBK) {
         const uint4 a0 = load16_guarded<kFast>(xrow, k0 + 32 * shalf, xlimit);
@@ -103,6 +116,16 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         *reinterpret_cast<uint4*>(As + srow * kLdA + 32 * shalf) = a0;
         *reinterpret_cast<uint4*>(As + srow * kLdA + 32 * shalf + 16) = a1;
         __syncthreads();
+        if constexpr (kTin) {
+            const uint4 wv = load16_guarded<kFast>(wbrow, k0 + 16 * (lane >> 4), K);
+            const v4i bt = {(int)wv.x, (int)wv.y, (int)wv.z, (int)wv.w};
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const v4i at = *reinterpret_cast<const v4i*>(As + (32 * wave + 16 * j + (lane & 15)) * kLdA +
+                                                             16 * (lane >> 4));
+                tacc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(at, bt, tacc[j], 0, 0, 0);
+            }
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             v4i af[2];
@@ -123,10 +146,25 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     // row sums of the codes, LoRA operands for this tile
     rs += __shfl_xor(rs, 1, kWave);
     if (shalf == 0) rowsum[srow] = rs;
+    if constexpr (kTin) {
+        // D[4 (lane >> 4) + v][lane & 15] = t[row 32 wave + 16 j + 4 (lane >> 4) + v][rank lane & 15]
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) tS[32 * wave + 16 * j + 4 * (lane >> 4) + v][lane & 15] = tacc[j][v];
+        __syncthreads();
+        if (t_out && rank != 0 && tile_n == 0) {
+            for (int e = tid; e < kBM * kRank; e += 256) {
+                const int64_t m = m0 + e / kRank;
+                if (m < M) t_out[m * kRank + e % kRank] = tS[e / kRank][e % kRank];
+            }
+        }
+    }
     for (int e = tid; e < kBM * kRank; e += 256) {
         const int r = e % kRank, row = e / kRank;
         const int64_t m = m0 + row;
-        uS[row][r] = (rank != 0 && m < M) ? s_b[r] * (float)t[m * kRank + r] : 0.0f;
+        const float tv = kTin ? (float)tS[row][r] : (rank != 0 && m < M) ? (float)t[m * kRank + r] : 0.0f;
+        uS[row][r] = (rank != 0 && m < M) ? s_b[r] * tv : 0.0f;
         const int64_t n = n0 + row;
         waS[row][r] = (rank != 0 && n < N) ? (float)w_a[n * kRank + r] : 0.0f;
     }
@@ -158,22 +196,33 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     }
 }
 
+// t given (w_b == NULL), or computed here from W_B (t_out, when not NULL, receives it).
 hipError_t launch_gemm_mfma(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                             const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
-                            const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                            int64_t batch, hipStream_t stream) {
+                            const int8_t* w_b, const float* s_b, const int32_t* t, int32_t* t_out, int rank,
+                            float* y, int32_t* acc_dbg, int64_t batch, hipStream_t stream) {
     const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
     const int64_t grid = tiles_m * tiles_n;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    const bool fast = (K % 64 == 0) && ((uintptr_t)x_q % 16 == 0) && ((uintptr_t)w_bits % 16 == 0);
+    const bool tin = rank != 0 && w_b != nullptr;
+    const bool fast = (K % 64 == 0) && ((uintptr_t)x_q % 16 == 0) && ((uintptr_t)w_bits % 16 == 0) &&
+                      (!tin || (uintptr_t)w_b % 16 == 0);
     const dim3 g3((unsigned)grid, (unsigned)batch);
+#define DFSSM_MFMA_LAUNCH(FAST, TIN)                                                                          \
+    gemm_mfma_kernel<FAST, TIN><<<g3, 256, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, \
+                                                        y, acc_dbg, tiles_n, w_b, t_out)
     if (fast) {
-        gemm_mfma_kernel<true><<<g3, 256, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b,
-                                                                 t, rank, y, acc_dbg, tiles_n);
+        if (tin) {
+            DFSSM_MFMA_LAUNCH(true, true);
+        } else {
+            DFSSM_MFMA_LAUNCH(true, false);
+        }
+    } else if (tin) {
+        DFSSM_MFMA_LAUNCH(false, true);
     } else {
-        gemm_mfma_kernel<false><<<g3, 256, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b,
-                                                                  t, rank, y, acc_dbg, tiles_n);
+        DFSSM_MFMA_LAUNCH(false, false);
     }
+#undef DFSSM_MFMA_LAUNCH
     return hipGetLastError();
 }
 

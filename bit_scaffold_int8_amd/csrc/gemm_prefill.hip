@@ -102,7 +102,9 @@ struct Args {
     const int8_t* w_a;
     const float* s_a;
     const float* s_b;
-    const int32_t* t;
+    const int32_t* t;     // given t (kTin = false)
+    const int8_t* w_b;    // W_B (kTin = true: t = W_B x_q computed in the K loop)
+    int32_t* t_out;       // kTin: optional copy of t (written by the first column tile)
     float* y;
     int32_t* acc_dbg;
     int M, N, K, rank;
@@ -137,13 +139,21 @@ __device__ __forceinline__ v8bf pack_bf16(const uint32_t (&b)[8]) {
     return __builtin_bit_cast(v8bf, w);
 }
 
-// One output tile of configuration C over the column range of `seg`.
-template <class C, bool kDebug>
+// One output tile of configuration C over the column range of `seg`.  kTin: the LoRA
+// down-projection t = W_B x_q is computed here, from the code chunks already in LDS, on
+// v_mfma_i32_16x16x64_i8 (A = 16 token rows, B = the 16 rows of W_B read from memory):
+// the waves of a K group share the tile's 16-row blocks, and the K groups' partial t
+// meet in LDS after the main loop.
+template <class C, bool kDebug, bool kTin>
 __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __restrict__ lds, int tile,
                                              const prefill::Seg& seg) {
     using namespace prefill;
     constexpr int MB = C::MB, NB = C::NB, KS = C::KS, WNW = C::WNW, BM = C::BM, WN = C::WN, BN = C::BN;
     constexpr int GS = C::GS, P = C::P, JB = C::JB, RBLK = C::RBLK;
+    // 16-row blocks of t per wave (every block once per K group)
+    constexpr int TB = (BM / 16 + WNW - 1) / WNW;
+    static_assert(TB * WNW == BM / 16, "t row blocks split evenly over a K group's waves");
+    static_assert(!kTin || KS * BM * kRank * 4 <= C::kABytes * 2, "t hand-over fits the chunk buffers");
     // code piece j is staged in step st_step(j) of a chunk
     auto st_step = [](int j) { return j * 4 / P; };
     const int M = a.M, N = a.N, K = a.K;
@@ -223,6 +233,28 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     };
     auto b_op = [](const v2u& bits, int s) -> v4i { return bits16((s < 2 ? bits.x : bits.y) >> (16 * (s & 1))); };
 
+    // kTin: W_B row (lane & 15) over k = c kChunk + 64 h + 16 (lane >> 4), h = 0, 1 (the
+    // B operand of the t MFMAs); chunks past the group's range or past K read zero
+    const bool lora = a.rank != 0;
+    const __amdgpu_buffer_rsrc_t wb_rsrc = make_rsrc(a.w_b, (kTin && lora) ? (uint32_t)(kRank * K) : 0u);
+    const int wb_lane = (lane & 15) * K + 16 * (lane >> 4);
+    auto wb_load = [&](int c, int h) -> v4i {
+        const int k = c * kChunk + 64 * h;
+        const bool live = kTin && c < c_end && k < K;
+        return __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(wb_rsrc, live ? wb_lane + k : kLoadDead, 0, 0));
+    };
+    // A operand of the t MFMAs: token rows 16 rb + (lane & 15) of block j, k-step h
+    auto ta_frag = [&](int buf, int j, int h) -> v4i {
+        const int rb = wn + WNW * j;
+        return *reinterpret_cast<const v4i*>(abuf + buf * C::kABytes + (16 * rb + (lane & 15)) * kLdA + 64 * h +
+                                             16 * (lane >> 4));
+    };
+    v4i tacc[kTin ? TB : 1];
+#pragma unroll
+    for (int j = 0; j < (kTin ? TB : 1); ++j) tacc[j] = (v4i){0, 0, 0, 0};
+    v4i wbv;  // the W_B piece of the next t k-step (one register set)
+
     v16i acc[MB][NB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -238,6 +270,7 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     for (int j = 0; j < P; ++j) stage[j] = st_load(c_begin, j);
 #pragma unroll
     for (int i = 0; i < JB; ++i) bst[i] = bs_load(0, i);
+    if constexpr (kTin) wbv = wb_load(c_begin, 0);
 #pragma unroll
     for (int j = 0; j < P; ++j) {
         *reinterpret_cast<v4i*>(abuf + st_loff[j]) = stage[j];
@@ -270,6 +303,9 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     // bits and chunk 2 stores them, a chunk before chunk 3 first reads them.  The one
     // barrier per chunk sits in step 3, after the last store and before the first read
     // of the next chunk; every read of the current buffers was issued before it.
+    // kTin: the t MFMAs of k-step h run in step h, beside the main MFMAs, on the current
+    // code buffer; the W_B piece of k-step 1 is loaded in step 0, and the next chunk's
+    // first piece in step 2 (one register set).
     auto chunk = [&](int b, int q, const v2u (&bc)[NB], v2u (&bn)[NB]) {
         const int c = c_begin + kBlk * b + q;
         const int cur = q & 1, nxt = cur ^ 1;
@@ -291,6 +327,15 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
             if (s == 1) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) bn[nb] = q < 3 ? b_bits(bb_cur, q + 1, nb) : b_bits(bb_cur ^ 1, 0, nb);
+            }
+            if constexpr (kTin) {
+                if (s < 2) {
+#pragma unroll
+                    for (int j = 0; j < TB; ++j)
+                        tacc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ta_frag(cur, j, s), wbv, tacc[j], 0, 0, 0);
+                }
+                if (s == 0) wbv = wb_load(c, 1);
+                if (s == 2) wbv = wb_load(c + 1, 0);
             }
             if (s == 3) {
                 if (q == 2) {
@@ -374,11 +419,34 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
         }
     }
 
+    // kTin: the K groups' partial t tiles, tl[kq][row][rank], in the chunk buffers (free
+    // now: their last reads came before the barriers above); D[4 (lane >> 4) + v][lane & 15]
+    // of block j is t[row 16 rb + 4 (lane >> 4) + v][rank lane & 15].
+    int32_t* const tl = reinterpret_cast<int32_t*>(lds);
+    if constexpr (kTin) {
+#pragma unroll
+        for (int j = 0; j < TB; ++j) {
+            const int rb = wn + WNW * j;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                tl[(kq * BM + 16 * rb + 4 * (lane >> 4) + v) * kRank + (lane & 15)] = tacc[j][v];
+        }
+        lds_barrier();
+        // the first column tile of each row block also writes t
+        if (a.t_out != nullptr && lora && seg.n_begin == 0 && tn == 0) {
+            for (int e = threadIdx.x; e < BM * kRank; e += C::NW * kWave) {
+                int32_t v = 0;
+#pragma unroll
+                for (int q = 0; q < KS; ++q) v += tl[q * BM * kRank + e];
+                if (e / kRank < rows) a.t_out[(int64_t)m0 * kRank + e] = v;
+            }
+        }
+    }
+
     // ---- epilogue: LoRA-up on bf16 MFMA, scales, stores ----
     // Every load and store below goes through a resource sized to this tile, so no
     // element needs a branch: rows past M fall past the y resource by construction,
     // columns past the range get kColDead added, and a missing LoRA reads as zeros.
-    const bool lora = a.rank != 0;
     const int N4 = N * 4;
     const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(a.y + (int64_t)m0 * N, (uint32_t)(rows * N4));
     const __amdgpu_buffer_rsrc_t d_rsrc =
@@ -390,7 +458,8 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     const __amdgpu_buffer_rsrc_t wa_rsrc =
         make_rsrc(lora ? a.w_a + (int64_t)ncl * kRank : a.w_a, lora ? (uint32_t)(cols * kRank) : 0u);
     const __amdgpu_buffer_rsrc_t t_rsrc =
-        make_rsrc(lora ? a.t + (int64_t)m0 * kRank : a.t, lora ? (uint32_t)(rows * kRank * 4) : 0u);
+        make_rsrc(lora && !kTin ? static_cast<const void*>(a.t + (int64_t)m0 * kRank) : static_cast<const void*>(a.s_x),
+                  lora && !kTin ? (uint32_t)(rows * kRank * 4) : 0u);
     const __amdgpu_buffer_rsrc_t sb_rsrc = make_rsrc(a.s_b, lora ? (uint32_t)(kRank * 4) : 0u);
 
     // per column block: this lane's column n0 + 32 nb + l32
@@ -453,8 +522,20 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
         v8bf uh, um, ul;
         if (lora) {
             const int off = ((32 * mb + l32) * kRank + 8 * g) * 4;
-            const v4u t0 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(t_rsrc, off, 0, 0));
-            const v4u t1 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(t_rsrc, off + 16, 0, 0));
+            v4u t0, t1;
+            if constexpr (kTin) {
+                // rows past M hold codes of zero, so their t is zero like a missing row's
+                t0 = *reinterpret_cast<const v4u*>(tl + (32 * mb + l32) * kRank + 8 * g);
+                t1 = *reinterpret_cast<const v4u*>(tl + (32 * mb + l32) * kRank + 8 * g + 4);
+#pragma unroll
+                for (int q = 1; q < KS; ++q) {
+                    t0 += *reinterpret_cast<const v4u*>(tl + (q * BM + 32 * mb + l32) * kRank + 8 * g);
+                    t1 += *reinterpret_cast<const v4u*>(tl + (q * BM + 32 * mb + l32) * kRank + 8 * g + 4);
+                }
+            } else {
+                t0 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(t_rsrc, off, 0, 0));
+                t1 = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(t_rsrc, off + 16, 0, 0));
+            }
             uint32_t h[8], m[8], l[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -495,7 +576,7 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
 // the rest C1 over seg1.  Segment 0's tiles are dealt to the 8 XCDs in contiguous runs
 // (workgroups go to XCDs round-robin), so the code rows and sign columns one XCD reads
 // stay in its L2.
-template <class C0, class C1, bool kDebug>
+template <class C0, class C1, bool kDebug, bool kTin>
 __global__ __launch_bounds__(C0::NW * kWave) __attribute__((amdgpu_waves_per_eu(C0::NW / 4 * C0::OCC, C0::NW / 4 * C0::OCC))) void
 gemm_prefill_kernel(prefill::Args a, prefill::Seg seg0, prefill::Seg seg1) {
     static_assert(C0::NW == C1::NW && C0::OCC == C1::OCC, "both parts of a launch use the same workgroup shape");
@@ -514,7 +595,12 @@ gemm_prefill_kernel(prefill::Args a, prefill::Seg seg0, prefill::Seg seg1) {
             a.w_a += p * N * kRank;
             a.s_a += p * N;
             a.s_b += p * kRank;
-            a.t += p * M * kRank;
+            if (kTin) {
+                a.w_b += p * kRank * K;
+                if (a.t_out) a.t_out += p * M * kRank;
+            } else {
+                a.t += p * M * kRank;
+            }
         }
     }
     const int T0 = seg0.tiles_m * seg0.tiles_n;
@@ -522,9 +608,9 @@ gemm_prefill_kernel(prefill::Args a, prefill::Seg seg0, prefill::Seg seg1) {
     if (b < T0) {
         const int xcd = b % 8, q8 = T0 / 8, r8 = T0 % 8;
         const int tile = xcd * q8 + min(xcd, r8) + b / 8;
-        prefill_tile<C0, kDebug>(a, lds, tile, seg0);
+        prefill_tile<C0, kDebug, kTin>(a, lds, tile, seg0);
     } else {
-        prefill_tile<C1, kDebug>(a, lds, b - T0, seg1);
+        prefill_tile<C1, kDebug, kTin>(a, lds, b - T0, seg1);
     }
 }
 
@@ -668,10 +754,17 @@ hipError_t launch2(const prefill::Args& a, const Seg& s0, const Seg& s1, int64_t
     const int64_t blocks = (int64_t)s0.tiles_m * s0.tiles_n + (int64_t)s1.tiles_m * s1.tiles_n;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks, (unsigned)batch);
+    const bool tin = a.rank != 0 && a.w_b != nullptr;
     if (a.acc_dbg) {
-        gemm_prefill_kernel<C0, C1, true><<<grid, C0::NW * kWave, 0, stream>>>(a, s0, s1);
+        if (tin) {
+            gemm_prefill_kernel<C0, C1, true, true><<<grid, C0::NW * kWave, 0, stream>>>(a, s0, s1);
+        } else {
+            gemm_prefill_kernel<C0, C1, true, false><<<grid, C0::NW * kWave, 0, stream>>>(a, s0, s1);
+        }
+    } else if (tin) {
+        gemm_prefill_kernel<C0, C1, false, true><<<grid, C0::NW * kWave, 0, stream>>>(a, s0, s1);
     } else {
-        gemm_prefill_kernel<C0, C1, false><<<grid, C0::NW * kWave, 0, stream>>>(a, s0, s1);
+        gemm_prefill_kernel<C0, C1, false, false><<<grid, C0::NW * kWave, 0, stream>>>(a, s0, s1);
     }
     return hipGetLastError();
 }
@@ -719,11 +812,15 @@ bool prefill_supported(int64_t M, int64_t N, int64_t K) {
            M * N < ((int64_t)1 << 40);
 }
 
+// t given (w_b == NULL), or computed in the K loop from W_B (t_out, when not NULL,
+// receives it).
 hipError_t launch_gemm_prefill(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                                const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
-                               const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                               int64_t batch, int force_cfg, int force_tail, hipStream_t stream) {
-    const prefill::Args a{x_q, s_x, w_bits, s_w, w_a, s_a, s_b, t, y, acc_dbg, (int)M, (int)N, (int)K, rank};
+                               const int8_t* w_b, const float* s_b, const int32_t* t, int32_t* t_out, int rank,
+                               float* y, int32_t* acc_dbg, int64_t batch, int force_cfg, int force_tail,
+                               hipStream_t stream) {
+    const prefill::Args a{x_q, s_x, w_bits, s_w, w_a, s_a, s_b, t, w_b, t_out, y, acc_dbg,
+                          (int)M, (int)N, (int)K, rank};
     const Plan p = plan_for(M, N, K, batch, force_cfg, force_tail);
     switch (p.main_cfg) {
         case 0: return launch_main<C441, C422, C412>(a, p, batch, stream);

@@ -32,15 +32,23 @@
 
 namespace dfssm {
 
-// Operands of the fused variant, which also quantizes the tokens and computes the LoRA
-// down-projection t = W_B x_q itself (one launch per projection).  Outputs x_q, s_x and
-// t are written by the first group of each problem; every group computes them alike.
+// Where a group's setup takes the tokens' codes and the LoRA down-projection from:
+//  kGivenT   x_q and t = W_B x_q are inputs (t from a LoRA-down call);
+//  kQuantize x is the input: the setup quantizes the tokens and computes t itself (the
+//            one-call form; x_q, s_x and t are outputs);
+//  kCodes    x_q is the input: the setup computes t = W_B x_q itself (t an optional
+//            output).
+// Outputs of the setup are written by the first group of each problem; every group
+// computes them alike.
+enum : int { kGivenT = 0, kQuantize = 1, kCodes = 2 };
+
+// Operands of the kQuantize and kCodes setups.
 struct FusedIO {
-    const float* x;     // fp32 [M][K]
+    const float* x;     // fp32 [M][K] (kQuantize)
     const int8_t* w_b;  // int8 [16][K] (rank 16) or unused
-    int8_t* x_q;        // int8 [M][K]  (out)
-    float* s_x;         // fp32 [M]     (out)
-    int32_t* t;         // int32 [M][16] (out, rank 16)
+    int8_t* x_q;        // int8 [M][K]  (out, kQuantize)
+    float* s_x;         // fp32 [M]     (out, kQuantize)
+    int32_t* t;         // int32 [M][16] (out, rank 16; may be NULL with kCodes)
 };
 
 // Rows one workgroup owns at most (their epilogue operands live in LDS): 2048 for the
@@ -50,19 +58,20 @@ constexpr int gemv_rows_cap(int W, int T) { return (W >= 8 && T >= 4) ? 2048 : 1
 
 // One lane group = 16 lanes; one chunk = 16 packed bytes = 128 k of one row.
 // W waves split K; C chunks per lane; T row tiles (16 rows each) per stage.
-// kFused: quantize x and compute t in the setup (x_q, s_x, t are then outputs; needs
-// the 16-byte path, one chunk per lane, M <= 4 and M K <= 1024 W).
-template <int W, int C, int T, bool kFast, bool kFused>
+// kSetup: kQuantize needs the 16-byte path, one chunk per lane, M <= 4 and
+// M K <= 1024 W; kCodes and kGivenT take any decode shape.
+template <int W, int C, int T, bool kFast, int kSetup>
 // One chunk per lane with 8 waves, or with 4 (except the fused 4-tile shape, which
 // needs more): held to 128 registers per lane, so that four waves share each SIMD (two
 // 8-wave groups, or four 4-wave groups, per CU); wider variants take what they need.
 __global__ __launch_bounds__(W * kWave)
-__attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || !kFused))) ? 4 : 1))) void gemv_kernel(
+__attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kSetup != kQuantize))) ? 4 : 1))) void gemv_kernel(
     const int8_t* __restrict__ x_q, const float* __restrict__ s_x, int M, int64_t N, int64_t K,
     const uint8_t* __restrict__ w_bits, const float* __restrict__ s_w,
     const int8_t* __restrict__ w_a, const float* __restrict__ s_a, const float* __restrict__ s_b,
     const int32_t* __restrict__ t, int rank, float* __restrict__ y, int32_t* __restrict__ acc_dbg,
     int64_t num_tiles, int stages_per_wg, FusedIO fio) {
+    constexpr bool kFused = kSetup == kQuantize;
     static_assert(!kFused || (kFast && C == 1), "the fused setup needs whole 128-k chunks, one per lane");
     // epilogue: thread -> one row of the stage (its W_A row, s_A, s_w are loaded once per
     // stage) and E of that row's tokens
@@ -90,7 +99,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || !k
     constexpr int kFusedMK = 1024 * W;  // largest M K the fused setup takes
     __shared__ __align__(16) uint32_t codes_lds[kFused ? kFusedMK / 4 : 1];
     __shared__ float amax_part[kFused ? W : 1][4];
-    __shared__ int32_t tsum[kFused ? 16 : 1][kRank];
+    __shared__ int32_t tsum[kSetup != kGivenT ? 16 : 1][kRank];
 
     // problem blockIdx.y of a dense batch (every operand advanced by its own size)
     {
@@ -379,10 +388,16 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || !k
         store_rows();
         // (u, xsum and the row operands are read after the first stage's barrier below)
     } else {
+        // kCodes: t = W_B x_q is summed into LDS by every wave; zero it first
+        if constexpr (kSetup == kCodes) {
+            for (int e = threadIdx.x; e < 16 * kRank; e += W * kWave) (&tsum[0][0])[e] = 0;
+            lds_barrier();
+        }
         // token scales and the LoRA down-projection: loaded now, stored to LDS after the
         // activation loads below have been issued too
         // (buffer loads: t past M tokens and every LoRA operand at rank 0 read zero)
-        const __amdgpu_buffer_rsrc_t t_rsrc = make_rsrc(t, rank != 0 ? (uint32_t)(M * kRank * 4) : 0u);
+        const __amdgpu_buffer_rsrc_t t_rsrc =
+            make_rsrc(t, (kSetup == kGivenT && rank != 0) ? (uint32_t)(M * kRank * 4) : 0u);
         const __amdgpu_buffer_rsrc_t sb_rsrc = make_rsrc(s_b, rank != 0 ? (uint32_t)(kRank * 4) : 0u);
         float tv[U], sbv[U];
 #pragma unroll
@@ -390,7 +405,9 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || !k
             const int e = threadIdx.x + q * W * kWave;
             const int tok = e / kRank, r = e % kRank;
             const bool live = e < 16 * kRank;  // tokens past M fall past t's range
-            tv[q] = (float)(int32_t)__builtin_amdgcn_raw_buffer_load_b32(t_rsrc, live ? 4 * (tok * kRank + r) : kOffDead, 0, 0);
+            tv[q] = kSetup == kGivenT ? (float)(int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                                            t_rsrc, live ? 4 * (tok * kRank + r) : kOffDead, 0, 0)
+                                      : 0.0f;
             sbv[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sb_rsrc, 4 * r, 0, 0));
         }
         // token scales past M read zero (buffer range of M floats)
@@ -409,6 +426,29 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || !k
         // multiple of 128 on the 16-byte path, so a chunk is wholly in or out of the row.
         const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(x_q, kFast ? (uint32_t)(M * K) : 0u);
         const int xoff = kFast ? i * (int)K : 0;
+        // kCodes: W_B row i (rank i) over the same k as token i's codes, the A operand of
+        // the t MFMAs (B = the codes in natural order): D[4g + v][i] = t[token i][rank 4g + v]
+        const int8_t* wb_p = kSetup == kCodes ? fio.w_b + (int64_t)blockIdx.y * kRank * K : x_q;
+        const __amdgpu_buffer_rsrc_t wb_rsrc =
+            make_rsrc(wb_p, (kSetup == kCodes && kFast) ? (uint32_t)(kRank * K) : 0u);
+        const uint8_t* wbrow = reinterpret_cast<const uint8_t*>(wb_p) + (int64_t)i * K;
+        v4i acc_t = {0, 0, 0, 0};
+        if constexpr (kSetup == kCodes && !kFast) {
+            // byte-gathering path (ragged K or unaligned rows): t in a pass of its own over
+            // this lane's chunks, so its registers are not held beside the activations'
+#pragma unroll 1
+            for (int c = 0; c < C; ++c) {
+                const int64_t kb = 128 * (((int64_t)c * W + wave) * 4 + g);
+#pragma unroll 1
+                for (int e = 0; e < 8; ++e) {
+                    const uint4 av = load16_guarded<false>(wbrow, kb + 16 * e, K);
+                    const uint4 bv = load16_guarded<false>(xrow, kb + 16 * e, xlimit);
+                    acc_t = __builtin_amdgcn_mfma_i32_16x16x64_i8((v4i){(int)av.x, (int)av.y, (int)av.z, (int)av.w},
+                                                                  (v4i){(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w},
+                                                                  acc_t, 0, 0, 0);
+                }
+            }
+        }
         if constexpr (C > 1) {
             load_first_row();
             prefetch_first_stages();
@@ -434,6 +474,14 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || !k
                 nat[4 * e + 2] = v.z;
                 nat[4 * e + 3] = v.w;
             }
+            // (the fast path issues all eight W_B pieces now, beside the activations)
+            v4i wbv[(kSetup == kCodes && kFast) ? 8 : 1];
+            if constexpr (kSetup == kCodes && kFast) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    wbv[e] = __builtin_amdgcn_raw_buffer_load_b128(
+                        wb_rsrc, kb < K ? (int)(i * K + kb + 16 * e) : kOffDead - 64, 0, 0);
+            }
             if constexpr (C == 1) {
                 __builtin_amdgcn_sched_barrier(0);  // the activation loads go out first
                 load_first_row();
@@ -442,6 +490,13 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || !k
             }
 #pragma unroll
             for (int e = 0; e < 32; ++e) xpart = byte_sum(nat[e], xpart);
+            if constexpr (kSetup == kCodes && kFast) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const v4i bv = {(int)nat[4 * e], (int)nat[4 * e + 1], (int)nat[4 * e + 2], (int)nat[4 * e + 3]};
+                    acc_t = __builtin_amdgcn_mfma_i32_16x16x64_i8(wbv[e], bv, acc_t, 0, 0, 0);
+                }
+            }
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
 #pragma unroll
@@ -456,16 +511,38 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || !k
                 }
             }
         }
-        // LoRA: u[tok][r] = s_B[r] * t[tok][r] (fp32), shared by every output row.
+        if constexpr (kSetup == kCodes) {
+            // the waves' partial t tiles meet in LDS (token lanes only)
+            if (i < M) {
 #pragma unroll
-        for (int q = 0; q < U; ++q) {
-            const int e = threadIdx.x + q * W * kWave;
-            u[e < 16 * kRank ? e : 16 * kRank] = sbv[q] * tv[q];
+                for (int v = 0; v < 4; ++v) atomicAdd(&tsum[i][4 * g + v], acc_t[v]);
+            }
+        } else {
+            // LoRA: u[tok][r] = s_B[r] * t[tok][r] (fp32), shared by every output row.
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                const int e = threadIdx.x + q * W * kWave;
+                u[e < 16 * kRank ? e : 16 * kRank] = sbv[q] * tv[q];
+            }
         }
         sxs[threadIdx.x < 16 ? threadIdx.x : 16] = sxv;
         xs_part[wave][lane] = xpart;
         for (int e = threadIdx.x; e < 2 * T * 16 * 20; e += W * kWave) (&red[0][0][0])[e] = 0;
         lds_barrier();
+        if constexpr (kSetup == kCodes) {
+            // u from the summed t; the problem's first group also writes t when asked to
+            const bool writer = blockIdx.x == 0 && fio.t != nullptr && rank != 0;
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                const int e = threadIdx.x + q * W * kWave;
+                if (e < 16 * kRank) {
+                    const int tok = e / kRank, r = e % kRank;
+                    const int32_t tt = tsum[tok][r];
+                    u[e] = tok < M ? sbv[q] * (float)tt : 0.0f;
+                    if (writer && tok < M) fio.t[((int64_t)blockIdx.y * M + tok) * kRank + r] = tt;
+                }
+            }
+        }
         if (threadIdx.x < 16) {
             int32_t s = 0;
             for (int w = 0; w < W; ++w)
@@ -581,85 +658,94 @@ static int64_t resident_groups(Kernel kernel, int threads) {
     return (int64_t)per_cu * cus;
 }
 
-template <int W, int C, int T, bool kFast, bool kFused>
+template <int W, int C, int T, bool kFast, int kSetup>
 static int64_t gemv_resident() {
-    static const int64_t n = resident_groups(gemv_kernel<W, C, T, kFast, kFused>, W * kWave);
+    static const int64_t n = resident_groups(gemv_kernel<W, C, T, kFast, kSetup>, W * kWave);
     return n;
 }
 
 template <int W, int C, int T>
-static hipError_t launch_gemv_wct(bool fast, const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
-                                  const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
-                                  const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                                  int64_t batch, const FusedIO* fio, hipStream_t stream) {
+static hipError_t launch_gemv_wct(bool fast, int setup, const int8_t* x_q, const float* s_x, int M, int64_t N,
+                                  int64_t K, const uint8_t* w_bits, const float* s_w, const int8_t* w_a,
+                                  const float* s_a, const float* s_b, const int32_t* t, int rank, float* y,
+                                  int32_t* acc_dbg, int64_t batch, const FusedIO& fio, hipStream_t stream) {
     const int64_t num_tiles = (N + 15) / 16;
     const int64_t num_stages = (num_tiles + T - 1) / T;
     // Large batches: one resident round of groups, each over as many rows as it can
     // hold, so the setup is paid once per group and no second round trails.  Otherwise
-    // ~8 groups per CU, or ~1 per CU for the fused variant, whose every group quantizes
-    // the tokens and reads all of W_B.
+    // ~8 groups per CU, or ~1 per CU for the setups that compute t, whose every group
+    // reads all of W_B (and, in the one-call form, quantizes the tokens).
     int64_t resident_wgs;
-    if constexpr (C == 1) {
-        resident_wgs = fio ? gemv_resident<W, C, T, true, true>()
-                           : fast ? gemv_resident<W, C, T, true, false>() : gemv_resident<W, C, T, false, false>();
+    if (setup == kQuantize) {
+        if constexpr (C == 1) {
+            resident_wgs = gemv_resident<W, C, T, true, kQuantize>();
+        } else {
+            return hipErrorNotSupported;
+        }
+    } else if (setup == kCodes) {
+        resident_wgs = fast ? gemv_resident<W, C, T, true, kCodes>() : gemv_resident<W, C, T, false, kCodes>();
     } else {
-        resident_wgs = fast ? gemv_resident<W, C, T, true, false>() : gemv_resident<W, C, T, false, false>();
+        resident_wgs = fast ? gemv_resident<W, C, T, true, kGivenT>() : gemv_resident<W, C, T, false, kGivenT>();
     }
     const bool throughput = batch * num_stages >= 4 * resident_wgs;
-    const int64_t target_wgs = throughput ? resident_wgs : (fio ? 256 : 2048);
+    const int64_t target_wgs = throughput ? resident_wgs : (setup != kGivenT ? 256 : 2048);
     const int64_t per_problem = (target_wgs + batch - 1) / batch;
     int stages_per_wg = (int)((num_stages + per_problem - 1) / per_problem);
     constexpr int kRowsCap = gemv_rows_cap(W, T);
     if (stages_per_wg * T * 16 > kRowsCap) stages_per_wg = kRowsCap / (T * 16);
     const dim3 grid((unsigned)((num_stages + stages_per_wg - 1) / stages_per_wg), (unsigned)batch);
-    // In the throughput regime the fused variant pays off only with one group per
+    // In the throughput regime the one-call form pays off only with one group per
     // problem: every further group would quantize the tokens and read W_B again.
-    if (fio && throughput && grid.x > 1) return hipErrorNotSupported;
-    if (fio) {
-        if constexpr (C == 1) {
-            gemv_kernel<W, C, T, true, true><<<grid, W * kWave, 0, stream>>>(
-                x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, num_tiles, stages_per_wg, *fio);
+    if (setup == kQuantize && throughput && grid.x > 1) return hipErrorNotSupported;
+#define DFSSM_GEMV_LAUNCH(FAST, SETUP)                                                                        \
+    gemv_kernel<W, C, T, FAST, SETUP><<<grid, W * kWave, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, \
+                                                                      s_b, t, rank, y, acc_dbg, num_tiles,      \
+                                                                      stages_per_wg, fio)
+    if (setup == kQuantize) {
+        if constexpr (C == 1) DFSSM_GEMV_LAUNCH(true, kQuantize);
+    } else if (setup == kCodes) {
+        if (fast) {
+            DFSSM_GEMV_LAUNCH(true, kCodes);
         } else {
-            return hipErrorNotSupported;
+            DFSSM_GEMV_LAUNCH(false, kCodes);
         }
     } else if (fast) {
-        gemv_kernel<W, C, T, true, false><<<grid, W * kWave, 0, stream>>>(
-            x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, num_tiles, stages_per_wg, FusedIO{});
+        DFSSM_GEMV_LAUNCH(true, kGivenT);
     } else {
-        gemv_kernel<W, C, T, false, false><<<grid, W * kWave, 0, stream>>>(
-            x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, num_tiles, stages_per_wg, FusedIO{});
+        DFSSM_GEMV_LAUNCH(false, kGivenT);
     }
+#undef DFSSM_GEMV_LAUNCH
     return hipGetLastError();
 }
 
 template <int W, int C>
-static hipError_t launch_gemv_wc(bool fast, const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
-                                 const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
-                                 const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                                 int64_t batch, const FusedIO* fio, hipStream_t stream) {
+static hipError_t launch_gemv_wc(bool fast, int setup, const int8_t* x_q, const float* s_x, int M, int64_t N,
+                                 int64_t K, const uint8_t* w_bits, const float* s_w, const int8_t* w_a,
+                                 const float* s_a, const float* s_b, const int32_t* t, int rank, float* y,
+                                 int32_t* acc_dbg, int64_t batch, const FusedIO& fio, hipStream_t stream) {
     // Few tiles overall (one decode call): one tile per stage spreads the rows over
     // the most CUs.  Many tiles (batched calls): four tiles per stage keep more
     // packed-sign loads in flight per wave.
     constexpr int kTBig = (W >= 4 && C <= 2) ? 4 : 1;
     const int64_t total_tiles = batch * ((N + 15) / 16);
     if (total_tiles <= 4096)
-        return launch_gemv_wct<W, C, 1>(fast, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg,
-                                        batch, fio, stream);
-    return launch_gemv_wct<W, C, kTBig>(fast, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg,
-                                        batch, fio, stream);
+        return launch_gemv_wct<W, C, 1>(fast, setup, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y,
+                                        acc_dbg, batch, fio, stream);
+    return launch_gemv_wct<W, C, kTBig>(fast, setup, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y,
+                                        acc_dbg, batch, fio, stream);
 }
 
 // Waves per group for rows of NC 16-byte chunks (zero: too long for the decode kernel).
 static int gemv_waves(int64_t NC) { return NC <= 4 ? 1 : NC <= 8 ? 2 : NC <= 16 ? 4 : NC <= 128 ? 8 : 0; }
 
-static hipError_t launch_gemv_any(bool fast, const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
-                                  const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
-                                  const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                                  int64_t batch, const FusedIO* fio, hipStream_t stream) {
+static hipError_t launch_gemv_any(bool fast, int setup, const int8_t* x_q, const float* s_x, int M, int64_t N,
+                                  int64_t K, const uint8_t* w_bits, const float* s_w, const int8_t* w_a,
+                                  const float* s_a, const float* s_b, const int32_t* t, int rank, float* y,
+                                  int32_t* acc_dbg, int64_t batch, const FusedIO& fio, hipStream_t stream) {
     const int64_t NC = (K / 8 + 15) / 16;  // 16-byte chunks per row
-#define DFSSM_GEMV(Wv, Cv) \
-    return launch_gemv_wc<Wv, Cv>(fast, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, \
-                                  fio, stream)
+#define DFSSM_GEMV(Wv, Cv)                                                                                       \
+    return launch_gemv_wc<Wv, Cv>(fast, setup, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, \
+                                  batch, fio, stream)
     if (NC <= 4) DFSSM_GEMV(1, 1);
     if (NC <= 8) DFSSM_GEMV(2, 1);
     if (NC <= 16) DFSSM_GEMV(4, 1);
@@ -671,14 +757,19 @@ static hipError_t launch_gemv_any(bool fast, const int8_t* x_q, const float* s_x
     return hipErrorInvalidValue;
 }
 
+// The decode kernel with t given (w_b == NULL) or, with rank 16 and w_b given, with
+// t = W_B x_q computed by every group (t_out, when not NULL, receives it).
 hipError_t launch_gemv(const int8_t* x_q, const float* s_x, int M, int64_t N, int64_t K,
                        const uint8_t* w_bits, const float* s_w, const int8_t* w_a, const float* s_a,
-                       const float* s_b, const int32_t* t, int rank, float* y, int32_t* acc_dbg,
-                       int64_t batch, hipStream_t stream) {
+                       const int8_t* w_b, const float* s_b, const int32_t* t, int32_t* t_out, int rank, float* y,
+                       int32_t* acc_dbg, int64_t batch, hipStream_t stream) {
     const int64_t RB = K / 8;
-    const bool fast = (RB % 16 == 0) && ((uintptr_t)w_bits % 16 == 0) && ((uintptr_t)x_q % 16 == 0);
-    return launch_gemv_any(fast, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, nullptr,
-                           stream);
+    const bool codes = rank != 0 && w_b != nullptr;
+    const bool fast = (RB % 16 == 0) && ((uintptr_t)w_bits % 16 == 0) && ((uintptr_t)x_q % 16 == 0) &&
+                      (!codes || (uintptr_t)w_b % 16 == 0);
+    const FusedIO fio{nullptr, w_b, nullptr, nullptr, t_out};
+    return launch_gemv_any(fast, codes ? kCodes : kGivenT, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank,
+                           y, acc_dbg, batch, fio, stream);
 }
 
 // Whether one launch can quantize, project down and run the scaffold product: whole
@@ -698,8 +789,8 @@ hipError_t launch_decode_fused(const float* x, int M, int64_t N, int64_t K, cons
     if (!decode_fused_supported(M, K) || (uintptr_t)w_bits % 16 != 0 || (uintptr_t)x % 16 != 0)
         return hipErrorNotSupported;
     const FusedIO fio{x, w_b, x_q, s_x, t};
-    return launch_gemv_any(true, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg, batch, &fio,
-                           stream);
+    return launch_gemv_any(true, kQuantize, x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, s_b, t, rank, y, acc_dbg,
+                           batch, fio, stream);
 }
 
 }  // namespace dfssm

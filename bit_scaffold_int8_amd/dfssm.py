@@ -21,7 +21,8 @@ DFSSM_ERR_HIP = 3
 EXPORTED = ("dfssm_status_string", "dfssm_version", "dfssm_quantize_act", "dfssm_lora_down",
             "dfssm_lora_down_strided_batched", "dfssm_quantize_lora_down",
             "dfssm_quantize_lora_down_strided_batched", "dfssm_scaffold_lora_gemm",
-            "dfssm_scaffold_lora_gemm_strided_batched", "dfssm_scaffold_lora_forward",
+            "dfssm_scaffold_lora_gemm_strided_batched", "dfssm_scaffold_lora_gemm_given_t",
+            "dfssm_scaffold_lora_gemm_given_t_strided_batched", "dfssm_scaffold_lora_forward",
             "dfssm_scaffold_lora_forward_strided_batched", "dfssm_int8_rowscale_gemm",
             "dfssm_int8_rowscale_gemm_strided_batched", "dfssm_embedding_lookup", "dfssm_mamba2_decode_step",
             "dfssm_prefill_plan")
@@ -48,8 +49,11 @@ def _load():
         "dfssm_lora_down_strided_batched": [P, i64, i64, P, i32, P, i64, P],
         "dfssm_quantize_lora_down": [P, i64, i64, P, i32, P, P, P, P],
         "dfssm_quantize_lora_down_strided_batched": [P, i64, i64, P, i32, P, P, P, i64, P],
-        "dfssm_scaffold_lora_gemm": [P, P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P],
-        "dfssm_scaffold_lora_gemm_strided_batched": [P, P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, i64, P],
+        "dfssm_scaffold_lora_gemm": [P, P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P, P],
+        "dfssm_scaffold_lora_gemm_strided_batched": [P, P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P, i64, P],
+        "dfssm_scaffold_lora_gemm_given_t": [P, P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P],
+        "dfssm_scaffold_lora_gemm_given_t_strided_batched": [P, P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, i64,
+                                                             P],
         "dfssm_scaffold_lora_forward": [P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P, P, P, P],
         "dfssm_scaffold_lora_forward_strided_batched": [P, i64, i64, i64, P, P, P, P, P, P, i32, P, P, P, P, P,
                                                         i64, P],
@@ -149,25 +153,49 @@ def dfssm_quantize_lora_down_strided_batched(x, w_b, x_q, s_x, t, stream=None) -
           _ptr(t), B, _stream(stream))
 
 
-def dfssm_scaffold_lora_gemm(x_q, s_x, w_bits, s_w, w_a, s_a, s_b, t, y, acc_dbg=None, stream=None) -> None:
-    """y fp32 [M, N] from x_q [M, K], s_x [M], w_bits [N, K/8], s_w [N] and the LoRA
-    operands w_a [N, 16], s_a [N], s_b [16], t [M, 16] (all None for rank 0)."""
+def dfssm_scaffold_lora_gemm(x_q, s_x, w_bits, s_w, w_a, s_a, w_b, s_b, y, acc_dbg=None, t_dbg=None,
+                             stream=None) -> None:
+    """y fp32 [M, N] from x_q [M, K], s_x [M], w_bits [N, K/8], s_w [N] and the LoRA pair
+    w_a [N, 16], s_a [N], w_b [16, K], s_b [16] (all None for rank 0); t = W_B x_q is
+    computed by the kernel (t_dbg [M, 16], when given, receives it)."""
     M, K = x_q.shape
     N = w_bits.shape[0]
     rank = 0 if w_a is None else int(w_a.shape[1])
     _call("dfssm_scaffold_lora_gemm", _ptr(x_q), _ptr(s_x), M, N, K, _ptr(w_bits), _ptr(s_w), _ptr(w_a),
-          _ptr(s_a), _ptr(s_b), _ptr(t), rank, _ptr(y), _ptr(acc_dbg), _stream(stream))
+          _ptr(s_a), _ptr(w_b), _ptr(s_b), rank, _ptr(y), _ptr(acc_dbg), _ptr(t_dbg), _stream(stream))
 
 
-def dfssm_scaffold_lora_gemm_strided_batched(x_q, s_x, w_bits, s_w, w_a, s_a, s_b, t, y, acc_dbg=None,
-                                             stream=None) -> None:
+def dfssm_scaffold_lora_gemm_strided_batched(x_q, s_x, w_bits, s_w, w_a, s_a, w_b, s_b, y, acc_dbg=None,
+                                             t_dbg=None, stream=None) -> None:
     """Batched form: x_q [B, M, K], s_x [B, M], w_bits [B, N, K/8], s_w [B, N], w_a [B, N, 16],
-    s_a [B, N], s_b [B, 16], t [B, M, 16], y [B, M, N]."""
+    s_a [B, N], w_b [B, 16, K], s_b [B, 16], y [B, M, N], t_dbg [B, M, 16]."""
     B, M, K = x_q.shape
     N = w_bits.shape[1]
     rank = 0 if w_a is None else int(w_a.shape[2])
     _call("dfssm_scaffold_lora_gemm_strided_batched", _ptr(x_q), _ptr(s_x), M, N, K, _ptr(w_bits), _ptr(s_w),
-          _ptr(w_a), _ptr(s_a), _ptr(s_b), _ptr(t), rank, _ptr(y), _ptr(acc_dbg), B, _stream(stream))
+          _ptr(w_a), _ptr(s_a), _ptr(w_b), _ptr(s_b), rank, _ptr(y), _ptr(acc_dbg), _ptr(t_dbg), B,
+          _stream(stream))
+
+
+def dfssm_scaffold_lora_gemm_given_t(x_q, s_x, w_bits, s_w, w_a, s_a, s_b, t, y, acc_dbg=None,
+                                     stream=None) -> None:
+    """The product with t [M, 16] given (from dfssm_lora_down / dfssm_quantize_lora_down):
+    y fp32 [M, N] from x_q, s_x, w_bits, s_w and w_a, s_a, s_b, t (all None for rank 0)."""
+    M, K = x_q.shape
+    N = w_bits.shape[0]
+    rank = 0 if w_a is None else int(w_a.shape[1])
+    _call("dfssm_scaffold_lora_gemm_given_t", _ptr(x_q), _ptr(s_x), M, N, K, _ptr(w_bits), _ptr(s_w), _ptr(w_a),
+          _ptr(s_a), _ptr(s_b), _ptr(t), rank, _ptr(y), _ptr(acc_dbg), _stream(stream))
+
+
+def dfssm_scaffold_lora_gemm_given_t_strided_batched(x_q, s_x, w_bits, s_w, w_a, s_a, s_b, t, y, acc_dbg=None,
+                                                     stream=None) -> None:
+    """Batched form of dfssm_scaffold_lora_gemm_given_t: every operand with a leading [B]."""
+    B, M, K = x_q.shape
+    N = w_bits.shape[1]
+    rank = 0 if w_a is None else int(w_a.shape[2])
+    _call("dfssm_scaffold_lora_gemm_given_t_strided_batched", _ptr(x_q), _ptr(s_x), M, N, K, _ptr(w_bits),
+          _ptr(s_w), _ptr(w_a), _ptr(s_a), _ptr(s_b), _ptr(t), rank, _ptr(y), _ptr(acc_dbg), B, _stream(stream))
 
 
 def dfssm_scaffold_lora_forward(x, w_bits, s_w, w_a, s_a, w_b, s_b, x_q, s_x, t, y, acc_dbg=None,

@@ -75,13 +75,30 @@ class DeviceProjections:
         dfssm.dfssm_quantize_lora_down_strided_batched(self.x, self.w_b, self.x_q, self.s_x, self.t, stream)
 
     def gemm(self, stream=None, debug: bool = True):
-        dfssm.dfssm_scaffold_lora_gemm_strided_batched(
+        """The product with t given (dfssm_scaffold_lora_gemm_given_t, after quantize_lora_down)."""
+        dfssm.dfssm_scaffold_lora_gemm_given_t_strided_batched(
             self.x_q, self.s_x, self.w_bits, self.s_w, self.w_a, self.s_a, self.s_b, self.t, self.y,
             self.acc_dbg if debug else None, stream)
 
     def forward(self, stream=None, debug: bool = True):
         self.quantize_lora_down(stream)
         self.gemm(stream, debug)
+
+    # ---- the specified two-call form: quantize, then the product computing t itself
+    def quantize(self, stream=None):
+        B, M, K = self.x.shape
+        dfssm.dfssm_quantize_act(self.x.view(B * M, K), self.x_q.view(B * M, K), self.s_x.view(B * M), stream)
+
+    def gemm_computing_t(self, stream=None, debug: bool = True):
+        """dfssm_scaffold_lora_gemm: t = W_B x_q inside the kernel (written to self.t when
+        debug and rank 16)."""
+        dfssm.dfssm_scaffold_lora_gemm_strided_batched(
+            self.x_q, self.s_x, self.w_bits, self.s_w, self.w_a, self.s_a, self.w_b, self.s_b, self.y,
+            self.acc_dbg if debug else None, self.t if debug else None, stream)
+
+    def forward_contract(self, stream=None, debug: bool = True):
+        self.quantize(stream)
+        self.gemm_computing_t(stream, debug)
 
     # ---- the one-call form (one launch at decode shapes)
     def forward_one_call(self, stream=None, debug: bool = True):
@@ -95,11 +112,23 @@ class DeviceProjections:
             dfssm.dfssm_quantize_act(self.x[b], self.x_q[b], self.s_x[b], stream)
             if self.rank:
                 dfssm.dfssm_lora_down(self.x_q[b], self.w_b[b], self.t[b], stream)
-            dfssm.dfssm_scaffold_lora_gemm(
+            dfssm.dfssm_scaffold_lora_gemm_given_t(
                 self.x_q[b], self.s_x[b], self.w_bits[b], self.s_w[b],
                 None if not self.rank else self.w_a[b], None if not self.rank else self.s_a[b],
                 None if not self.rank else self.s_b[b], None if not self.rank else self.t[b], self.y[b],
                 None if (self.acc_dbg is None or not debug) else self.acc_dbg[b], stream)
+
+    def forward_contract_unfused(self, stream=None, debug: bool = True):
+        """Problem by problem through the single-problem entry points of the specified
+        form: dfssm_quantize_act, then dfssm_scaffold_lora_gemm (t computed inside)."""
+        for b in range(self.B):
+            dfssm.dfssm_quantize_act(self.x[b], self.x_q[b], self.s_x[b], stream)
+            dfssm.dfssm_scaffold_lora_gemm(
+                self.x_q[b], self.s_x[b], self.w_bits[b], self.s_w[b],
+                None if not self.rank else self.w_a[b], None if not self.rank else self.s_a[b],
+                None if not self.rank else self.w_b[b], None if not self.rank else self.s_b[b], self.y[b],
+                None if (self.acc_dbg is None or not debug) else self.acc_dbg[b],
+                None if (not self.rank or not debug) else self.t[b], stream)
 
 
 @dataclass

@@ -16,12 +16,14 @@
  *   y[m][n]   = s_x[m] * ( s_w[n] * acc[m][n]
  *                          + s_A[n] * sum_r W_A[n][r] * s_B[r] * t[m][r] )   (fp32)
  *
- * A forward step is one call, dfssm_scaffold_lora_forward (x -> x_q, s_x, t, y), or
- * two: dfssm_quantize_lora_down (x -> x_q, s_x, t) and dfssm_scaffold_lora_gemm
+ * A forward step is dfssm_quantize_act (x -> x_q, s_x) followed by
+ * dfssm_scaffold_lora_gemm (x_q, s_x, W, W_A, W_B -> y, t computed inside), or one
+ * call, dfssm_scaffold_lora_forward (x -> x_q, s_x, t, y), or the split form
+ * dfssm_quantize_lora_down (x -> x_q, s_x, t) then dfssm_scaffold_lora_gemm_given_t
  * (x_q, s_x, t -> y).  The LoRA down-projection t is a reduction over all of K that
- * every output needs; the two-call form produces it before the main kernel, which
- * then runs without any cross-workgroup dependency, and the one-call form has every
- * workgroup of a decode-shaped call compute it (and the codes) for itself.
+ * every output needs: dfssm_scaffold_lora_gemm has every workgroup compute the part of
+ * it that its outputs need (no cross-workgroup dependency, no scratch memory), and the
+ * split form produces it before the main kernel.
  *
  * Data layout (all row-major, contiguous, device memory):
  *   x      fp32  [M][K]
@@ -131,44 +133,78 @@ dfssm_status dfssm_quantize_lora_down_strided_batched(const float* x, int64_t M,
                                                       hipStream_t stream);
 
 /*
- * Scaffold product with the fused scale + LoRA-up epilogue (technical summary
- * sections 2B and 2C): y = s_x . (s_w . (W x_q) + s_A . W_A (s_B . t)).
- *   x_q, s_x     quantized activations (dfssm_quantize_act)
- *   w_bits, s_w  the 1-bit scaffold and its per-output-channel scale
- *   w_a, s_a, s_b, t, rank  the LoRA up factor, its scales and t = W_B x_q
- *                (dfssm_lora_down); rank 16, or 0 for no correction (then
- *                w_a, s_a, s_b, t may be NULL)
+ * Scaffold product with the fused LoRA + scale epilogue (technical summary section 2B,
+ * "Frozen Scaffold with LoRA Correction": W_A d_out x r, W_B r x d_in, r = 16, int8 with
+ * per-row scales; section 2C, "Optimized Inference Pipeline": packed 1-bit weights
+ * expanded on the fly to int8 for an int8 x int8 product):
+ *   t   = W_B x_q                                       (exact int32, computed here)
+ *   y   = s_x . (s_w . (W x_q) + s_A . W_A (s_B . t))
+ *   x_q, s_x     int8 [M][K] and fp32 [M]: quantized activations (dfssm_quantize_act)
+ *   w_bits, s_w  the 1-bit scaffold [N][K/8] and its per-output-channel scale [N]
+ *   w_a, s_a     LoRA up, int8 [N][rank] and fp32 [N]
+ *   w_b, s_b     LoRA down, int8 [rank][K] and fp32 [rank]
+ *   rank         16, or 0 for no correction (then w_a, s_a, w_b, s_b may be NULL)
  *   y            fp32 [M][N], written
- *   acc_dbg      optional int32 [M][N]: when not NULL, also receives the exact
- *                scaffold accumulators sum_k w x_q (verification aid)
+ *   acc_dbg      optional int32 [M][N]: when not NULL, also receives the exact scaffold
+ *                accumulators sum_k w x_q (verification aid; NULL in timed runs)
+ *   t_dbg        optional int32 [M][rank]: when not NULL (rank 16), also receives t
+ *                (verification aid; NULL in timed runs)
  * Requires M, N >= 1, K >= 8, K % 8 == 0, K <= 131072.  M <= 16 (with K <= 16384)
- * runs the bandwidth-bound decode kernel, otherwise an int8 MFMA kernel (tile
- * configuration chosen by a cost model of the shape; K % 64 != 0 takes a generic
- * fallback kernel); either way one kernel launch.  For tests and tuning, the
- * environment variable DFSSM_PREFILL_CFG pins the MFMA kernel's tile configuration
- * (0, 1, ...; -2 = the generic kernel) and DFSSM_PREFILL_TAIL a narrower one for the
- * columns past the pinned one's main part, where the pinned configuration is built
- * with that tail (otherwise every column runs on the pinned one); results are the
- * same either way.
+ * runs the bandwidth-bound decode kernel, whose every workgroup computes t for the
+ * tokens from W_B (16 K bytes, L2-resident) before streaming its rows; otherwise an int8
+ * MFMA kernel (tile configuration chosen by a cost model of the shape; K % 64 != 0
+ * takes a generic fallback kernel) computes each tile's rows of t inside its K loop,
+ * from the code chunks it already stages.  Either way one kernel launch and no scratch
+ * memory.  For tests and tuning, the environment variable DFSSM_PREFILL_CFG pins the
+ * MFMA kernel's tile configuration (0, 1, ...; -2 = the generic kernel) and
+ * DFSSM_PREFILL_TAIL a narrower one for the columns past the pinned one's main part,
+ * where the pinned configuration is built with that tail (otherwise every column runs
+ * on the pinned one); results are the same either way.
+ * Errors: DFSSM_ERR_INVALID_ARG for a NULL x_q, s_x, w_bits, s_w or y, for a NULL w_a,
+ * s_a, w_b or s_b at rank 16, for sizes out of range or K % 8 != 0, and for
+ * misaligned pointers; DFSSM_ERR_UNSUPPORTED for rank other than 0 and 16 or
+ * K > 131072; DFSSM_ERR_HIP for a failed launch.  Nothing is launched on an error.
  */
-dfssm_status dfssm_scaffold_lora_gemm(const int8_t* x_q, const float* s_x,
-                                      int64_t M, int64_t N, int64_t K,
+dfssm_status dfssm_scaffold_lora_gemm(const int8_t* x_q, const float* s_x, int64_t M, int64_t N, int64_t K,
                                       const uint8_t* w_bits, const float* s_w,
-                                      const int8_t* w_a, const float* s_a, const float* s_b,
-                                      const int32_t* t, int32_t rank,
-                                      float* y, int32_t* acc_dbg, hipStream_t stream);
+                                      const int8_t* w_a, const float* s_a,
+                                      const int8_t* w_b, const float* s_b, int32_t rank,
+                                      float* y, int32_t* acc_dbg, int32_t* t_dbg, hipStream_t stream);
 dfssm_status dfssm_scaffold_lora_gemm_strided_batched(const int8_t* x_q, const float* s_x,
                                                       int64_t M, int64_t N, int64_t K,
                                                       const uint8_t* w_bits, const float* s_w,
-                                                      const int8_t* w_a, const float* s_a, const float* s_b,
-                                                      const int32_t* t, int32_t rank,
-                                                      float* y, int32_t* acc_dbg,
+                                                      const int8_t* w_a, const float* s_a,
+                                                      const int8_t* w_b, const float* s_b, int32_t rank,
+                                                      float* y, int32_t* acc_dbg, int32_t* t_dbg,
                                                       int64_t batch, hipStream_t stream);
+
+/*
+ * The same product with t given (technical summary sections 2B and 2C): t = W_B x_q
+ * from dfssm_lora_down or dfssm_quantize_lora_down, so the kernel reads t instead of
+ * W_B.  Results are bit-identical to dfssm_scaffold_lora_gemm on the same x_q.
+ *   w_a, s_a, s_b, t, rank  the LoRA up factor, its scales and t int32 [M][rank];
+ *                rank 16, or 0 for no correction (then w_a, s_a, s_b, t may be NULL)
+ * Other arguments, requirements and errors as dfssm_scaffold_lora_gemm (a NULL t at
+ * rank 16 is DFSSM_ERR_INVALID_ARG).
+ */
+dfssm_status dfssm_scaffold_lora_gemm_given_t(const int8_t* x_q, const float* s_x,
+                                              int64_t M, int64_t N, int64_t K,
+                                              const uint8_t* w_bits, const float* s_w,
+                                              const int8_t* w_a, const float* s_a, const float* s_b,
+                                              const int32_t* t, int32_t rank,
+                                              float* y, int32_t* acc_dbg, hipStream_t stream);
+dfssm_status dfssm_scaffold_lora_gemm_given_t_strided_batched(const int8_t* x_q, const float* s_x,
+                                                              int64_t M, int64_t N, int64_t K,
+                                                              const uint8_t* w_bits, const float* s_w,
+                                                              const int8_t* w_a, const float* s_a,
+                                                              const float* s_b, const int32_t* t, int32_t rank,
+                                                              float* y, int32_t* acc_dbg,
+                                                              int64_t batch, hipStream_t stream);
 
 /*
  * The whole projection in one call (technical summary sections 2B and 2C; the
  * formulas above): x -> x_q, s_x, t and y, with the same results, bit for bit, as
- * dfssm_quantize_lora_down followed by dfssm_scaffold_lora_gemm.
+ * dfssm_quantize_lora_down followed by dfssm_scaffold_lora_gemm_given_t.
  *   x                      fp32 [M][K], read
  *   w_bits, s_w            the scaffold and its scale
  *   w_a, s_a, w_b, s_b     the LoRA pair and its scales (rank 16), or rank 0 with

@@ -166,3 +166,12 @@ CONFIGS = {
     # gated RMS norm): 64 heads x 64 channels, state 128, at 1 and 64 sequences
     "mamba2_decode_step": dict(sequences=[1, 64], seed=6),
 }
+
+
+def prefill_problems() -> list[Problem]:
+    """The M = 2048 prefill workload: in_proj (K 2048 -> N 8512), then out_proj
+    (K 4096 -> N 2048), drawn back to back from one stream seeded as the workload says."""
+    cfg = CONFIGS["prefill_m2048"]
+    rng = np.random.default_rng(cfg["seed"])
+    return [draw_problem(rng, *shape) for shape in cfg["shapes"]]
+

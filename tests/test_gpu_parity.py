@@ -25,16 +25,28 @@ def torch_cuda():
     return torch
 
 
+PATHS = ("fused", "contract")
+
+
 def _run_hip(prob, with_acc=True, rank=16, path="fused"):
-    """Run one problem through the C ABI; path 'fused' = quantize_lora_down + gemm
-    (batched entry points, batch 1), 'unfused' = quantize_act, lora_down, gemm."""
+    """Run one problem through the C ABI:
+    'fused'    quantize_lora_down + gemm_given_t (batched entry points, batch 1);
+    'unfused'  quantize_act, lora_down, gemm_given_t (single-problem entry points);
+    'contract' quantize_act + scaffold_lora_gemm, which computes t itself (batched);
+    'contract_unfused' the same through the single-problem entry points."""
     from bit_scaffold_int8_amd.runner import DeviceProjections
     import torch
     dp = DeviceProjections.from_problems([prob], rank=bool(rank), with_acc=with_acc)
     if path == "fused":
         dp.forward()
-    else:
+    elif path == "unfused":
         dp.forward_unfused()
+    elif path == "contract":
+        dp.forward_contract()
+    elif path == "contract_unfused":
+        dp.forward_contract_unfused()
+    else:
+        raise ValueError(path)
     torch.cuda.synchronize()
     out = dict(x_q=dp.x_q[0].cpu().numpy(), s_x=dp.s_x[0].cpu().numpy(), y=dp.y[0].cpu().numpy())
     if rank:
@@ -82,21 +94,24 @@ def _check_full(prob, rank=16, nthreads=8, path="fused"):
 
 # ------------------------------------------------------------------ the five workloads
 
-def test_tiny_m1_k256_n512(torch_cuda):
+@pytest.mark.parametrize("path", PATHS)
+def test_tiny_m1_k256_n512(torch_cuda, path):
     (M, N, K, o), = si.CONFIGS["tiny_m1_k256_n512"]["shapes"]
-    _check_full(si.make_problem(M, N, K, o, seed=0))
+    _check_full(si.make_problem(M, N, K, o, seed=0), path=path)
 
 
-def test_out_proj_decode_m1_k4096_n2048(torch_cuda):
+@pytest.mark.parametrize("path", PATHS)
+def test_out_proj_decode_m1_k4096_n2048(torch_cuda, path):
     (M, N, K, o), = si.CONFIGS["out_proj_decode_m1_k4096_n2048"]["shapes"]
     # several rotated copies from the same stream, as the benchmark draws them
     for prob in si.make_copies(M, N, K, o, seed=1, copies=3):
-        _check_full(prob)
+        _check_full(prob, path=path)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("M", [1, 4, 16])
-def test_in_proj_decode_k2048_n8512(torch_cuda, M):
-    _check_full(si.make_problem(M, 8512, 2048, 2, seed=2))
+def test_in_proj_decode_k2048_n8512(torch_cuda, M, path):
+    _check_full(si.make_problem(M, 8512, 2048, 2, seed=2), path=path)
 
 
 def test_decode_sweep_48_layers_sampled(torch_cuda):
@@ -113,10 +128,7 @@ def test_decode_sweep_48_layers_sampled(torch_cuda):
 
 @pytest.mark.parametrize("which", [0, 1])
 def test_prefill_m2048_sampled(torch_cuda, which):
-    cfg = si.CONFIGS["prefill_m2048"]
-    rng = np.random.default_rng(cfg["seed"])
-    probs = [si.draw_problem(rng, *s) for s in cfg["shapes"]]
-    prob = probs[which]
+    prob = si.prefill_problems()[which]
     got = _run_hip(prob)
     xq_ref, sx_ref = oracle.quantize_act(prob.x)
     assert np.array_equal(got["s_x"].view(np.uint32), sx_ref.view(np.uint32))
@@ -152,9 +164,10 @@ def test_prefill_m2048_sampled(torch_cuda, which):
 
 # ------------------------------------------------------------------ edge shapes
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("M", [1, 2, 3, 15, 16, 17, 127, 128, 129])
-def test_token_counts(torch_cuda, M):
-    _check_full(si.make_problem(M, 100, 2048, 2, seed=1000 + M))
+def test_token_counts(torch_cuda, M, path):
+    _check_full(si.make_problem(M, 100, 2048, 2, seed=1000 + M), path=path)
 
 
 @pytest.mark.parametrize("M,N,K", [
@@ -162,20 +175,24 @@ def test_token_counts(torch_cuda, M):
     (17, 1, 8), (17, 63, 40), (33, 70, 1000), (129, 65, 520), (200, 130, 136), (64, 129, 4104),
     (1, 64, 16384), (2, 40, 16392), (1, 300, 12288),
 ])
-def test_ragged_shapes(torch_cuda, M, N, K):
-    _check_full(si.make_problem(M, N, K, 2 if K >= 16 else 0, seed=M * 7 + N * 3 + K))
+@pytest.mark.parametrize("path", PATHS)
+def test_ragged_shapes(torch_cuda, M, N, K, path):
+    _check_full(si.make_problem(M, N, K, 2 if K >= 16 else 0, seed=M * 7 + N * 3 + K), path=path)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("M", [1, 5, 40])
-def test_rank_zero(torch_cuda, M):
-    _check_full(si.make_problem(M, 96, 1024, 2, seed=77 + M), rank=0)
+def test_rank_zero(torch_cuda, M, path):
+    _check_full(si.make_problem(M, 96, 1024, 2, seed=77 + M), rank=0, path=path)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 2048, 4096), (4, 300, 2048), (16, 64, 1000), (40, 90, 520),
                                    (2, 70, 72), (1, 33, 65536)])
-def test_unfused_entry_points(torch_cuda, M, N, K):
-    # quantize_act, lora_down and gemm called one by one
-    _check_full(si.make_problem(M, N, K, 2, seed=5 * M + K), path="unfused")
+@pytest.mark.parametrize("path", ["unfused", "contract_unfused"])
+def test_unfused_entry_points(torch_cuda, M, N, K, path):
+    # the single-problem entry points called one by one: quantize_act, lora_down and
+    # gemm_given_t, or quantize_act and scaffold_lora_gemm (t computed inside)
+    _check_full(si.make_problem(M, N, K, 2, seed=5 * M + K), path=path)
 
 
 @pytest.mark.parametrize("M,K", [(1, 65536), (3, 65544), (2, 131072)])
@@ -202,12 +219,13 @@ def test_quantize_act_any_row_length(torch_cuda, M, K):
 
 
 @pytest.mark.parametrize("B,M,N,K", [(5, 1, 2048, 4096), (3, 4, 8512, 2048), (4, 33, 100, 1024), (7, 2, 40, 136)])
-def test_strided_batched_matches_oracle_per_problem(torch_cuda, B, M, N, K):
+@pytest.mark.parametrize("path", PATHS)
+def test_strided_batched_matches_oracle_per_problem(torch_cuda, B, M, N, K, path):
     import torch
     from bit_scaffold_int8_amd.runner import DeviceProjections
     probs = si.make_copies(M, N, K, 2, seed=B * 1000 + K, copies=B)
     dp = DeviceProjections.from_problems(probs, with_acc=True)
-    dp.forward()
+    dp.forward() if path == "fused" else dp.forward_contract()
     torch.cuda.synchronize()
     for b, prob in enumerate(probs):
         xq_ref, sx_ref = oracle.quantize_act(prob.x)
@@ -221,7 +239,8 @@ def test_strided_batched_matches_oracle_per_problem(torch_cuda, B, M, N, K):
 
 
 @pytest.mark.parametrize("B,M,N,K", [(512, 1, 2048, 4096), (200, 3, 2000, 4096), (300, 16, 1024, 2048)])
-def test_large_batches_one_group_round(torch_cuda, B, M, N, K):
+@pytest.mark.parametrize("path", PATHS)
+def test_large_batches_one_group_round(torch_cuda, B, M, N, K, path):
     # batches large enough that the decode kernel gives each group a whole problem (or
     # an even share of one) in a single resident round: the benchmark's launch (512
     # out_proj copies), ragged rows with an uneven split, and 16 tokens on 4-wave groups
@@ -229,7 +248,7 @@ def test_large_batches_one_group_round(torch_cuda, B, M, N, K):
     from bit_scaffold_int8_amd.runner import DeviceProjections
     probs = si.make_copies(M, N, K, 2, seed=B + N + K, copies=B)
     dp = DeviceProjections.from_problems(probs, with_acc=True)
-    dp.forward()
+    dp.forward() if path == "fused" else dp.forward_contract()
     torch.cuda.synchronize()
     acc_all, y_all, t_all = dp.acc_dbg.cpu().numpy(), dp.y.cpu().numpy(), dp.t.cpu().numpy()
     for b, prob in enumerate(probs):
@@ -242,18 +261,30 @@ def test_large_batches_one_group_round(torch_cuda, B, M, N, K):
         _assert_y(y_all[b], y_ref, D, f"batch {b}")
 
 
-def test_gemm_without_debug_output_gives_same_y(torch_cuda):
+@pytest.mark.parametrize("path", PATHS)
+def test_gemm_without_debug_output_gives_same_y(torch_cuda, path):
     import torch
     from bit_scaffold_int8_amd.runner import DeviceProjections
     for (M, N, K) in [(1, 2048, 4096), (300, 200, 512)]:
         dp = DeviceProjections.from_problems([si.make_problem(M, N, K, 2, seed=3)], with_acc=True)
-        dp.forward(debug=True)
+        fwd = dp.forward if path == "fused" else dp.forward_contract
+        fwd(debug=True)
         torch.cuda.synchronize()
         y1 = dp.y.clone()
         dp.y.zero_()
-        dp.forward(debug=False)
+        fwd(debug=False)
         torch.cuda.synchronize()
         assert torch.equal(y1, dp.y)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 2048, 4096), (5, 300, 2048), (40, 200, 1024), (3, 33, 200)])
+def test_contract_matches_given_t_bitwise(torch_cuda, M, N, K):
+    # t computed inside the product (scaffold_lora_gemm) and t given (quantize_lora_down
+    # + scaffold_lora_gemm_given_t) produce the same bytes
+    a = _run_hip(si.make_problem(M, N, K, 2, seed=M + N + K), path="fused")
+    b = _run_hip(si.make_problem(M, N, K, 2, seed=M + N + K), path="contract")
+    for k in ("x_q", "s_x", "t", "acc", "y"):
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
 
 
 def test_zero_token_and_exact_ties(torch_cuda):
