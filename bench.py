@@ -164,6 +164,8 @@ def parse():
     ap.add_argument("--prefill-iters", type=int, default=10)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMV traffic record from two rocprofv3 counter_collection.csv files")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the 48-layer decode legs (persistent one-launch and per-call chain)")
     ap.add_argument("--mamba2-only", action="store_true",
                     help="only the Mamba-2 step legs and the copy probe (counter runs of the step kernels)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -420,6 +422,40 @@ def decode_chain_48l(torch, dev, replays):
                     "out_proj (one-call), each reading the previous one's output"}
 
 
+def decode_persistent_48l(torch, dev, tokens):
+    """The same decode as decode_chain_48l (48 x (in_proj -> Mamba-2 step -> out_proj) at
+    one sequence), as ONE launch per token (dfssm_decode_layers: a persistent grid with
+    device-wide counters between the steps).  Tokens back to back, the windows swapped
+    each token, the state carried; every call's status word must stay clear."""
+    import synth_inputs as si
+    from bit_scaffold_int8_amd.runner import DeviceDecodeStack
+    cfg = si.CONFIGS["decode_sweep_48l"]
+    st = si.draw_decode_stack(np.random.default_rng(cfg["seed"] + 200), cfg["layers"])
+    d = DeviceDecodeStack(st, device=dev)
+    x = torch.from_numpy(st.x).to(dev)
+    x_out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    it = iter(range(10 ** 9))
+
+    def token():
+        d.step(x, x_out, parity=next(it) % 2, stream=stream)
+    for _ in range(10):
+        token()
+    torch.cuda.synchronize()
+    ms = time_events(torch, token, tokens, stream)
+    status = int(d.status.item())
+    (Mi, Ni, Ki, _), (Mo, No, Ko, _) = cfg["shapes"]
+    token_bytes = cfg["layers"] * (step_bytes(Mi, Ni, Ki) + step_bytes(Mo, No, Ko) + mamba2_step_bytes(1))
+    del d
+    return {"layers": cfg["layers"], "launches_per_token": 1, "bytes_per_token": token_bytes,
+            "us_per_token": round(ms * 1e3, 1), "GBps": round(token_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(token_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tokens_timed": tokens, "status": status,
+            "note": "dfssm_decode_layers: one cooperative launch of 256 x 512 threads per token; per layer "
+                    "in_proj, Mamba-2 step, gated norm + out_proj, separated by device-wide counters; weights "
+                    "and state prefetched while waiting"}
+
+
 def mfma_probe():
     """int8 MFMA rate this GPU sustains on given operand data (libdfssm_probe.so)."""
     import ctypes
@@ -533,6 +569,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    if args.decode_only:
+        print(json.dumps({"decode_persistent_48l": decode_persistent_48l(torch, dev, 128),
+                          "decode_chain_48l": decode_chain_48l(torch, dev, 64)}))
+        return
     if args.mamba2_only:
         print(json.dumps({"mamba2_decode_step": mamba2_step_bench(torch, dev, args.steps),
                           "probes": probes(torch, stream)}))
@@ -721,6 +761,8 @@ def main():
         if not args.no_sweeps:
             out["decode_chain_48l"] = decode_chain_48l(torch, dev, 64)    # 64 two-token replays
             progress("48-layer chain")
+            out["decode_persistent_48l"] = decode_persistent_48l(torch, dev, 128)
+            progress("48-layer one-launch decode")
         out["lm_head_decode_v50280_d2048"] = lm_head_decode(torch, dev, stream, args.steps, args.warmup)
         progress("LM head")
         out["probes"] = probes(torch, stream)

@@ -13,7 +13,7 @@ LIB = os.path.join(PKG, "libdfssm.so")
 PROBE_LIB = os.path.join(PKG, "libdfssm_probe.so")
 PROBE_SOURCES = ["probe_mfma.hip"]
 SOURCES = ["api.hip", "quantize.hip", "lora_down.hip", "gemv.hip", "gemm_mfma.hip", "gemm_prefill.hip",
-           "int8_head.hip", "mamba2_step.hip"]
+           "int8_head.hip", "mamba2_step.hip", "decode_layers.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -38,6 +38,9 @@ hipError_t launch_mamba2_step(const float* zxbcdt, int64_t S, int nheads, const 
                               float* ssm_state, const float* conv_w, const float* conv_b, const float* dt_bias,
                               const float* A_log, const float* D, const float* norm_w, float eps, float* out,
                               hipStream_t stream);
+size_t decode_layers_workspace_bytes();
+int64_t decode_layers_trace_words();
+int64_t decode_layers_max_layers();
 bool prefill_supported(int64_t M, int64_t N, int64_t K);
 int prefill_num_cfgs();
 void prefill_plan_query(int64_t M, int64_t N, int64_t K, int64_t batch, int* main_cfg, int* tail_cfg,
@@ -48,6 +51,8 @@ hipError_t launch_gemm_prefill(const int8_t* x_q, const float* s_x, int64_t M, i
                                float* y, int32_t* acc_dbg, int64_t batch, int force_cfg, int force_tail,
                                hipStream_t stream);
 }  // namespace dfssm
+
+#include "decode_args.h"
 
 namespace {
 
@@ -215,6 +220,43 @@ dfssm_status int8_head_impl(const int8_t* x_q, const float* s_x, int64_t M, int6
                : DFSSM_ERR_HIP;
 }
 
+dfssm_status decode_layers_impl(const dfssm_decode_layer_weights* w, int64_t n_layers, const float* x_in,
+                                float* x_out, const float* conv_in, float* conv_out, float* ssm_state, float eps,
+                                void* workspace, size_t workspace_bytes, int32_t* status, uint32_t* trace,
+                                int64_t spin_limit, uint32_t flags, hipStream_t stream) {
+    if (!w || !x_in || !x_out || !conv_in || !conv_out || !ssm_state || !workspace || !status)
+        return DFSSM_ERR_INVALID_ARG;
+    if (!w->in_w_bits || !w->in_s_w || !w->in_w_a || !w->in_s_a || !w->in_w_b || !w->in_s_b || !w->conv_w ||
+        !w->conv_b || !w->dt_bias || !w->A_log || !w->D || !w->norm_w || !w->out_w_bits || !w->out_s_w ||
+        !w->out_w_a || !w->out_s_a || !w->out_w_b || !w->out_s_b)
+        return DFSSM_ERR_INVALID_ARG;
+    if (n_layers < 1 || n_layers > dfssm::decode_layers_max_layers()) return DFSSM_ERR_INVALID_ARG;
+    if (!(eps >= 0.0f) || eps > 1e30f) return DFSSM_ERR_INVALID_ARG;
+    if (workspace_bytes < dfssm::decode_layers_workspace_bytes()) return DFSSM_ERR_INVALID_ARG;
+    if (flags & ~DFSSM_DECODE_UNREACHABLE_WAITS) return DFSSM_ERR_INVALID_ARG;
+    if (!aligned16(w->in_w_bits) || !aligned16(w->in_w_a) || !aligned16(w->in_w_b) || !aligned16(w->conv_w) ||
+        !aligned16(w->norm_w) || !aligned16(w->out_w_bits) || !aligned16(w->out_w_a) || !aligned16(w->out_w_b) ||
+        !aligned4(w->in_s_w) || !aligned4(w->in_s_a) || !aligned4(w->in_s_b) || !aligned4(w->conv_b) ||
+        !aligned4(w->dt_bias) || !aligned4(w->A_log) || !aligned4(w->D) || !aligned4(w->out_s_w) ||
+        !aligned4(w->out_s_a) || !aligned4(w->out_s_b) || !aligned16(x_in) || !aligned4(x_out) ||
+        !aligned16(conv_in) || !aligned16(conv_out) || !aligned16(ssm_state) || !aligned16(workspace) ||
+        !aligned4(status) || !aligned4_or_null(trace))
+        return DFSSM_ERR_INVALID_ARG;
+    const int64_t conv_bytes = n_layers * 4352 * 16;
+    const uintptr_t ci = (uintptr_t)conv_in, co = (uintptr_t)conv_out;
+    if (ci < co + (uintptr_t)conv_bytes && co < ci + (uintptr_t)conv_bytes) return DFSSM_ERR_INVALID_ARG;
+    const dfssm::decode::Args a{w->in_w_bits, w->in_s_w, w->in_w_a, w->in_s_a, w->in_w_b, w->in_s_b,
+                                w->conv_w, w->conv_b, w->dt_bias, w->A_log, w->D, w->norm_w,
+                                w->out_w_bits, w->out_s_w, w->out_w_a, w->out_s_a, w->out_w_b, w->out_s_b,
+                                conv_in, conv_out, ssm_state, x_in, x_out, trace,
+                                static_cast<uint32_t*>(workspace), status, (int)n_layers, eps,
+                                spin_limit > 0 ? spin_limit : ((int64_t)1 << 22),
+                                (flags & DFSSM_DECODE_UNREACHABLE_WAITS) ? (1u << 30) : 0u};
+    const hipError_t e = dfssm::launch_decode_layers(a, stream);
+    if (e == hipErrorNotSupported) return DFSSM_ERR_UNSUPPORTED;
+    return e == hipSuccess ? DFSSM_OK : DFSSM_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -356,6 +398,18 @@ dfssm_status dfssm_embedding_lookup(const int32_t* tokens, int64_t T, const int8
     if (V * K >= ((int64_t)1 << 40) || T * K >= ((int64_t)1 << 40)) return DFSSM_ERR_UNSUPPORTED;
     return dfssm::launch_embedding_lookup(tokens, T, e, s_e, V, K, out, stream) == hipSuccess ? DFSSM_OK
                                                                                             : DFSSM_ERR_HIP;
+}
+
+size_t dfssm_decode_layers_workspace_bytes(void) { return dfssm::decode_layers_workspace_bytes(); }
+
+int64_t dfssm_decode_layers_trace_words(void) { return dfssm::decode_layers_trace_words(); }
+
+dfssm_status dfssm_decode_layers(const dfssm_decode_layer_weights* w, int64_t n_layers, const float* x_in,
+                                 float* x_out, const float* conv_state_in, float* conv_state_out, float* ssm_state,
+                                 float eps, void* workspace, size_t workspace_bytes, int32_t* status, uint32_t* trace,
+                                 int64_t spin_limit, uint32_t flags, hipStream_t stream) {
+    return decode_layers_impl(w, n_layers, x_in, x_out, conv_state_in, conv_state_out, ssm_state, eps, workspace,
+                              workspace_bytes, status, trace, spin_limit, flags, stream);
 }
 
 dfssm_status dfssm_mamba2_decode_step(const float* zxbcdt, int64_t S, int64_t nheads, int64_t headdim,

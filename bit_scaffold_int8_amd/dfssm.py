@@ -25,7 +25,21 @@ EXPORTED = ("dfssm_status_string", "dfssm_version", "dfssm_quantize_act", "dfssm
             "dfssm_scaffold_lora_gemm_given_t_strided_batched", "dfssm_scaffold_lora_forward",
             "dfssm_scaffold_lora_forward_strided_batched", "dfssm_int8_rowscale_gemm",
             "dfssm_int8_rowscale_gemm_strided_batched", "dfssm_embedding_lookup", "dfssm_mamba2_decode_step",
-            "dfssm_prefill_plan")
+            "dfssm_prefill_plan", "dfssm_decode_layers_workspace_bytes", "dfssm_decode_layers_trace_words",
+            "dfssm_decode_layers")
+
+DFSSM_DECODE_STATUS_TIMEOUT = 1
+DFSSM_DECODE_STATUS_GAVE_UP = 2
+DFSSM_DECODE_UNREACHABLE_WAITS = 1
+
+# dfssm_decode_layer_weights: the stacked per-layer weights of dfssm_decode_layers
+DECODE_WEIGHT_FIELDS = ("in_w_bits", "in_s_w", "in_w_a", "in_s_a", "in_w_b", "in_s_b", "conv_w", "conv_b",
+                        "dt_bias", "A_log", "D", "norm_w", "out_w_bits", "out_s_w", "out_w_a", "out_s_a",
+                        "out_w_b", "out_s_b")
+
+
+class DecodeLayerWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in DECODE_WEIGHT_FIELDS]
 
 
 class DfssmError(RuntimeError):
@@ -43,6 +57,10 @@ def _load():
     lib.dfssm_status_string.restype = ctypes.c_char_p
     lib.dfssm_version.argtypes = []
     lib.dfssm_version.restype = i32
+    lib.dfssm_decode_layers_workspace_bytes.argtypes = []
+    lib.dfssm_decode_layers_workspace_bytes.restype = ctypes.c_size_t
+    lib.dfssm_decode_layers_trace_words.argtypes = []
+    lib.dfssm_decode_layers_trace_words.restype = i64
     sigs = {
         "dfssm_quantize_act": [P, i64, i64, P, P, P],
         "dfssm_lora_down": [P, i64, i64, P, i32, P, P],
@@ -62,6 +80,8 @@ def _load():
         "dfssm_embedding_lookup": [P, i64, P, P, i64, i64, P, P],
         "dfssm_mamba2_decode_step": [P, i64, i64, i64, i64, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P],
         "dfssm_prefill_plan": [i64, i64, i64, i64, P, P, P],
+        "dfssm_decode_layers": [P, i64, P, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t, P, P, i64, ctypes.c_uint32,
+                                P],
     }
     for name, argtypes in sigs.items():
         f = getattr(lib, name)
@@ -253,3 +273,25 @@ def dfssm_mamba2_decode_step(zxbcdt, conv_state_in, conv_state_out, ssm_state, c
     _call("dfssm_mamba2_decode_step", _ptr(zxbcdt), S, nheads, headdim, d_state, _ptr(conv_state_in),
           _ptr(conv_state_out), _ptr(ssm_state), _ptr(conv_w), _ptr(conv_b), _ptr(dt_bias), _ptr(A_log), _ptr(D),
           _ptr(norm_w), float(eps), _ptr(out), _stream(stream))
+
+
+def dfssm_decode_layers_workspace_bytes() -> int:
+    return int(lib.dfssm_decode_layers_workspace_bytes())
+
+
+def dfssm_decode_layers_trace_words() -> int:
+    return int(lib.dfssm_decode_layers_trace_words())
+
+
+def dfssm_decode_layers(weights: dict, n_layers, x_in, x_out, conv_state_in, conv_state_out, ssm_state, eps,
+                        workspace, status, trace=None, spin_limit: int = 0, flags: int = 0, stream=None) -> None:
+    """The decode step of n_layers stacked layers for one sequence, one launch.  `weights`
+    maps every name of DECODE_WEIGHT_FIELDS to a device tensor (stacked over layers);
+    workspace is a zeroed device buffer of dfssm_decode_layers_workspace_bytes() bytes,
+    status a device int32 the kernel ORs failure bits into."""
+    w = DecodeLayerWeights(*[_ptr(weights[name]) for name in DECODE_WEIGHT_FIELDS])
+    nbytes = workspace.numel() * workspace.element_size()
+    _call("dfssm_decode_layers", ctypes.addressof(w), int(n_layers), _ptr(x_in), _ptr(x_out), _ptr(conv_state_in),
+          _ptr(conv_state_out), _ptr(ssm_state), float(eps), _ptr(workspace), nbytes, _ptr(status), _ptr(trace),
+          int(spin_limit), int(flags), _stream(stream))
+

@@ -165,3 +165,43 @@ class DeviceMamba2Layer:
         dfssm.dfssm_mamba2_decode_step(zxbcdt, self.windows[parity], self.windows[1 - parity], self.ssm_state,
                                        self.conv_w, self.conv_b, self.dt_bias, self.A_log, self.D, self.norm_w,
                                        self.eps, self.out, stream)
+
+
+# host array name in a DecodeStack -> weight field of the persistent decode entry point
+DECODE_HOST_NAMES = {
+    "in_w_bits": "in_P", "in_s_w": "in_s_w", "in_w_a": "in_W_A", "in_s_a": "in_s_A", "in_w_b": "in_W_B",
+    "in_s_b": "in_s_B", "conv_w": "conv_w", "conv_b": "conv_b", "dt_bias": "dt_bias", "A_log": "A_log", "D": "D",
+    "norm_w": "norm_w", "out_w_bits": "out_P", "out_s_w": "out_s_w", "out_w_a": "out_W_A", "out_s_a": "out_s_A",
+    "out_w_b": "out_W_B", "out_s_b": "out_s_B",
+}
+
+
+class DeviceDecodeStack:
+    """A stack of layers on the device for dfssm_decode_layers: the stacked weights, the
+    two window buffers (a token reads one and writes the other), the SSM state (updated
+    in place), the counters' workspace (zeroed once here; every call leaves it zeroed)
+    and the status word."""
+
+    def __init__(self, stack, device="cuda:0", eps: float = 1e-5):
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        self.L = stack.L
+        self.weights = {k: dev(getattr(stack, v)) for k, v in DECODE_HOST_NAMES.items()}
+        w0 = dev(stack.conv_state)
+        self.windows = [w0, torch.empty_like(w0)]
+        self.ssm_state = dev(stack.ssm_state)
+        self.eps = eps
+        nbytes = dfssm.dfssm_decode_layers_workspace_bytes()
+        self.workspace = torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.trace_words = dfssm.dfssm_decode_layers_trace_words()
+
+    def new_trace(self):
+        return torch.empty((self.L, self.trace_words), dtype=torch.int32, device=self.ssm_state.device)
+
+    def step(self, x_in, x_out, parity: int = 0, trace=None, spin_limit: int = 0, flags: int = 0, stream=None):
+        """One token through every layer: windows[parity] -> windows[1 - parity]."""
+        dfssm.dfssm_decode_layers(self.weights, self.L, x_in, x_out, self.windows[parity], self.windows[1 - parity],
+                                  self.ssm_state, self.eps, self.workspace, self.status, trace, spin_limit, flags,
+                                  stream)
+

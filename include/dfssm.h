@@ -302,6 +302,93 @@ dfssm_status dfssm_mamba2_decode_step(const float* zxbcdt, int64_t S, int64_t nh
                                       const float* dt_bias, const float* A_log, const float* D,
                                       const float* norm_w, float eps, float* out, hipStream_t stream);
 
+/*
+ * The decode step of a stack of n_layers DF-SSM layers for one sequence (one token), in
+ * ONE kernel launch (technical summary section 2C, "Optimized Inference Pipeline": the
+ * whole 48-layer forward is captured as one graph because launch overhead decides
+ * batch-1 speed).  Per layer l, with the layer's input x (fp32 [2048]):
+ *   zxbcdt = scaffold_lora(quantize(x); in_proj weights of l)       (K 2048 -> N 8512)
+ *   out    = Mamba-2 step of dfssm_mamba2_decode_step (64 heads x 64 channels,
+ *            d_state 128, eps) on zxbcdt, with layer l's windows and state
+ *   x'     = scaffold_lora(quantize(out); out_proj weights of l)    (K 4096 -> N 2048)
+ * and x' is layer l + 1's input; x_out receives the last layer's x'.  Every arithmetic
+ * step is the one the single-projection entry points and dfssm_mamba2_decode_step
+ * define (the same quantizer, exact int32 products, the same fp32 epilogue and step).
+ * Model sizes are fixed to Mamba-2 1.3B's: d_model 2048, d_inner 4096, 64 heads,
+ * d_state 128, convolution width 4, in_proj width 8512.
+ *
+ * Weights (device memory, densely stacked over the layers; layer l's block follows
+ * layer l - 1's; 16-byte aligned where a row is read as a vector: the bits, W_A, W_B,
+ * conv_w, norm_w):
+ *   in_w_bits uint8 [L][8512][256]  in_s_w fp32 [L][8512]  in_w_a int8 [L][8512][16]
+ *   in_s_a fp32 [L][8512]  in_w_b int8 [L][16][2048]  in_s_b fp32 [L][16]
+ *   conv_w fp32 [L][4352][4]  conv_b, dt_bias, A_log, D fp32 [L][4352], [L][64] x 3
+ *   norm_w fp32 [L][4096]
+ *   out_w_bits uint8 [L][2048][512]  out_s_w fp32 [L][2048]  out_w_a int8 [L][2048][16]
+ *   out_s_a fp32 [L][2048]  out_w_b int8 [L][16][4096]  out_s_b fp32 [L][16]
+ * State and activations (device memory):
+ *   x_in  fp32 [2048] (16-byte aligned), read;  x_out fp32 [2048], written (may alias x_in)
+ *   conv_state_in [L][4352][4] read, conv_state_out [L][4352][4] written (16-byte
+ *     aligned, must not overlap: the caller swaps them between tokens)
+ *   ssm_state fp32 [L][64][64][128], updated in place (16-byte aligned)
+ *   trace  optional uint32 [L][dfssm_decode_layers_trace_words()]: when not NULL, each
+ *     layer's intermediates, at these word offsets: zxbcdt fp32 [8512] at 0, out fp32
+ *     [4096] at 8512, x' fp32 [2048] at 12608, in_proj accumulators int32 [8512] at
+ *     14656, out_proj accumulators int32 [2048] at 23168, x_q of x int8 [2048] at 25216,
+ *     x_q of out int8 [4096] at 25728, t of in_proj int32 [16] at 26752, t of out_proj
+ *     int32 [16] at 26768, s_x of x and of out fp32 at 26784 and 26785 (verification aid)
+ * Synchronization between the layer's three steps is device-wide counters in
+ * `workspace` (>= dfssm_decode_layers_workspace_bytes() bytes, 16-byte aligned, zeroed
+ * by the caller once before its first use; every call leaves it zeroed again).  Calls
+ * that share a workspace must not overlap (the same stream serializes them).
+ *   status     int32 in device memory: each wait that gives up ORs a bit in --
+ *              DFSSM_DECODE_STATUS_TIMEOUT (its poll limit passed) or
+ *              DFSSM_DECODE_STATUS_GAVE_UP (another group had failed); outputs are
+ *              then unspecified.  The kernel never hangs: every wait is bounded.  The
+ *              caller clears it; the library only ORs into it.
+ *   spin_limit polls per wait before it gives up (<= 0: 1 << 22, far beyond any wait
+ *              of a healthy run)
+ *   flags      0, or DFSSM_DECODE_UNREACHABLE_WAITS (a test aid: every wait's target is
+ *              unreachable, so every wait times out and the kernel still ends)
+ * Requires 1 <= n_layers <= 64 and eps >= 0.  DFSSM_ERR_UNSUPPORTED when the device
+ * cannot hold the persistent grid (256 co-resident 512-thread groups in a cooperative
+ * launch: MI355X's 256 CUs); DFSSM_ERR_INVALID_ARG for a NULL or misaligned pointer, a
+ * short workspace, overlapping windows or sizes out of range.  One launch on `stream`,
+ * nothing allocated; not for HIP graph capture (a cooperative launch).
+ */
+typedef struct dfssm_decode_layer_weights {
+    const uint8_t* in_w_bits;
+    const float* in_s_w;
+    const int8_t* in_w_a;
+    const float* in_s_a;
+    const int8_t* in_w_b;
+    const float* in_s_b;
+    const float* conv_w;
+    const float* conv_b;
+    const float* dt_bias;
+    const float* A_log;
+    const float* D;
+    const float* norm_w;
+    const uint8_t* out_w_bits;
+    const float* out_s_w;
+    const int8_t* out_w_a;
+    const float* out_s_a;
+    const int8_t* out_w_b;
+    const float* out_s_b;
+} dfssm_decode_layer_weights;
+
+#define DFSSM_DECODE_STATUS_TIMEOUT 1
+#define DFSSM_DECODE_STATUS_GAVE_UP 2
+#define DFSSM_DECODE_UNREACHABLE_WAITS 1u
+
+size_t dfssm_decode_layers_workspace_bytes(void);
+int64_t dfssm_decode_layers_trace_words(void);
+dfssm_status dfssm_decode_layers(const dfssm_decode_layer_weights* w, int64_t n_layers,
+                                 const float* x_in, float* x_out,
+                                 const float* conv_state_in, float* conv_state_out, float* ssm_state,
+                                 float eps, void* workspace, size_t workspace_bytes, int32_t* status,
+                                 uint32_t* trace, int64_t spin_limit, uint32_t flags, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -175,3 +175,61 @@ def prefill_problems() -> list[Problem]:
     rng = np.random.default_rng(cfg["seed"])
     return [draw_problem(rng, *shape) for shape in cfg["shapes"]]
 
+
+@dataclass
+class DecodeStack:
+    """A stack of L layers' decode weights and state for one sequence (host arrays,
+    stacked over layers in the layout the persistent decode entry point reads)."""
+    in_P: np.ndarray       # uint8 [L, 8512, 256]
+    in_s_w: np.ndarray     # float32 [L, 8512]
+    in_W_A: np.ndarray     # int8 [L, 8512, 16]
+    in_s_A: np.ndarray     # float32 [L, 8512]
+    in_W_B: np.ndarray     # int8 [L, 16, 2048]
+    in_s_B: np.ndarray     # float32 [L, 16]
+    conv_w: np.ndarray     # float32 [L, 4352, 4]
+    conv_b: np.ndarray     # float32 [L, 4352]
+    dt_bias: np.ndarray    # float32 [L, 64]
+    A_log: np.ndarray      # float32 [L, 64]
+    D: np.ndarray          # float32 [L, 64]
+    norm_w: np.ndarray     # float32 [L, 4096]
+    out_P: np.ndarray      # uint8 [L, 2048, 512]
+    out_s_w: np.ndarray    # float32 [L, 2048]
+    out_W_A: np.ndarray    # int8 [L, 2048, 16]
+    out_s_A: np.ndarray    # float32 [L, 2048]
+    out_W_B: np.ndarray    # int8 [L, 16, 4096]
+    out_s_B: np.ndarray    # float32 [L, 16]
+    conv_state: np.ndarray  # float32 [L, 4352, 4]
+    ssm_state: np.ndarray   # float32 [L, 64, 64, 128]
+    x: np.ndarray           # float32 [2048]: the first layer's input
+
+    @property
+    def L(self):
+        return self.in_P.shape[0]
+
+    def layer(self, l):
+        """Layer l's Mamba-2 parameters as a Mamba2Layer."""
+        return Mamba2Layer(self.conv_w[l], self.conv_b[l], self.dt_bias[l], self.A_log[l], self.D[l], self.norm_w[l])
+
+
+def draw_decode_stack(rng: np.random.Generator, L: int) -> DecodeStack:
+    """Per layer, in order: the in_proj weights (draw_problem at M = 1, K 2048 -> N 8512, no
+    outliers; its x is discarded), the Mamba-2 parameters (draw_mamba2_layer), the layer's
+    windows and state (draw_mamba2_inputs at one sequence; its zxbcdt is discarded), the
+    out_proj weights (draw_problem, K 4096 -> N 2048); then the first layer's input
+    x ~ N(0, 1)."""
+    ins, mls, convs, ssms, outs = [], [], [], [], []
+    for _ in range(L):
+        ins.append(draw_problem(rng, 1, 8512, 2048, 0))
+        mls.append(draw_mamba2_layer(rng))
+        _, conv, ssm = draw_mamba2_inputs(rng, 1)
+        convs.append(conv[0])
+        ssms.append(ssm[0])
+        outs.append(draw_problem(rng, 1, 2048, 4096, 0))
+    x = rng.standard_normal(2048, dtype=np.float32)
+    st = lambda items, name: np.ascontiguousarray(np.stack([getattr(i, name) for i in items]))  # noqa: E731
+    return DecodeStack(st(ins, "P"), st(ins, "s_w"), st(ins, "W_A"), st(ins, "s_A"), st(ins, "W_B"), st(ins, "s_B"),
+                       st(mls, "conv_w"), st(mls, "conv_b"), st(mls, "dt_bias"), st(mls, "A_log"), st(mls, "D"),
+                       st(mls, "norm_w"), st(outs, "P"), st(outs, "s_w"), st(outs, "W_A"), st(outs, "s_A"),
+                       st(outs, "W_B"), st(outs, "s_B"), np.ascontiguousarray(np.stack(convs)),
+                       np.ascontiguousarray(np.stack(ssms)), x)
+
