@@ -39,6 +39,7 @@ hipError_t launch_mamba2_step(const float* zxbcdt, int64_t S, int nheads, const 
                               const float* A_log, const float* D, const float* norm_w, float eps, float* out,
                               hipStream_t stream);
 size_t decode_layers_workspace_bytes();
+uint32_t* decode_layers_scratch(hipStream_t stream);
 int64_t decode_layers_trace_words();
 int64_t decode_layers_max_layers();
 bool prefill_supported(int64_t M, int64_t N, int64_t K);
@@ -223,7 +224,7 @@ dfssm_status int8_head_impl(const int8_t* x_q, const float* s_x, int64_t M, int6
 dfssm_status decode_layers_impl(const dfssm_decode_layer_weights* w, int64_t n_layers, const float* x_in,
                                 float* x_out, const float* conv_in, float* conv_out, float* ssm_state, float eps,
                                 void* workspace, size_t workspace_bytes, int32_t* status, uint32_t* trace,
-                                int64_t spin_limit, uint32_t flags, hipStream_t stream) {
+                                int64_t spin_limit, uint32_t flags, hipStream_t stream, bool validate_only = false) {
     if (!w || !x_in || !x_out || !conv_in || !conv_out || !ssm_state || !workspace || !status)
         return DFSSM_ERR_INVALID_ARG;
     if (!w->in_w_bits || !w->in_s_w || !w->in_w_a || !w->in_s_a || !w->in_w_b || !w->in_s_b || !w->conv_w ||
@@ -245,6 +246,7 @@ dfssm_status decode_layers_impl(const dfssm_decode_layer_weights* w, int64_t n_l
     const int64_t conv_bytes = n_layers * 4352 * 16;
     const uintptr_t ci = (uintptr_t)conv_in, co = (uintptr_t)conv_out;
     if (ci < co + (uintptr_t)conv_bytes && co < ci + (uintptr_t)conv_bytes) return DFSSM_ERR_INVALID_ARG;
+    if (validate_only) return DFSSM_OK;
     const dfssm::decode::Args a{w->in_w_bits, w->in_s_w, w->in_w_a, w->in_s_a, w->in_w_b, w->in_s_b,
                                 w->conv_w, w->conv_b, w->dt_bias, w->A_log, w->D, w->norm_w,
                                 w->out_w_bits, w->out_s_w, w->out_w_a, w->out_s_a, w->out_w_b, w->out_s_b,
@@ -403,6 +405,23 @@ dfssm_status dfssm_embedding_lookup(const int32_t* tokens, int64_t T, const int8
 size_t dfssm_decode_layers_workspace_bytes(void) { return dfssm::decode_layers_workspace_bytes(); }
 
 int64_t dfssm_decode_layers_trace_words(void) { return dfssm::decode_layers_trace_words(); }
+
+dfssm_status dfssm_decode_layers_noalloc(const dfssm_decode_layer_weights* w, int64_t n_layers, const float* x_in,
+                                         float* x_out, const float* conv_state_in, float* conv_state_out,
+                                         float* ssm_state, float eps, int32_t* status, uint32_t* trace,
+                                         int64_t spin_limit, uint32_t flags, hipStream_t stream) {
+    // the same checks as dfssm_decode_layers, with the library's array standing in for
+    // the workspace (a stand-in address passes them; the real one is fetched after)
+    alignas(16) static char probe[16];
+    if (dfssm_status st = decode_layers_impl(w, n_layers, x_in, x_out, conv_state_in, conv_state_out, ssm_state, eps,
+                                             probe, dfssm::decode_layers_workspace_bytes(), status, trace, spin_limit,
+                                             flags, stream, /*validate_only=*/true))
+        return st;
+    uint32_t* ws = dfssm::decode_layers_scratch(stream);
+    if (ws == nullptr) return DFSSM_ERR_HIP;
+    return decode_layers_impl(w, n_layers, x_in, x_out, conv_state_in, conv_state_out, ssm_state, eps, ws,
+                              dfssm::decode_layers_workspace_bytes(), status, trace, spin_limit, flags, stream, false);
+}
 
 dfssm_status dfssm_decode_layers(const dfssm_decode_layer_weights* w, int64_t n_layers, const float* x_in,
                                  float* x_out, const float* conv_state_in, float* conv_state_out, float* ssm_state,

@@ -38,6 +38,8 @@
 #include "device_common.h"
 #include "quant_common.h"
 
+#include <mutex>
+
 namespace dfssm {
 
 namespace decode {
@@ -568,6 +570,40 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
 }  // namespace dfssm
 
 namespace dfssm {
+
+namespace {
+
+// The no-allocation entry point's workspace: one array per GPU, held until the process
+// ends.  In host code `scratch` only names the variable; its device address comes from
+// hipGetSymbolAddress, once per device.
+__device__ __align__(256) uint32_t scratch[decode::kWsWords];
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+uint32_t* scratch_ptr[kMaxDevices];
+
+}  // namespace
+
+// The current device's scratch array: its address is taken (and its counters cleared on
+// `stream`) the first time a device is seen.  nullptr on a HIP error.
+uint32_t* decode_layers_scratch(hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+        // the counters must start at zero (every call leaves them so)
+        zero_words_kernel<<<16, 256, 0, stream>>>(static_cast<uint32_t*>(ptr), decode::kWsX);
+        if (hipGetLastError() != hipSuccess) return nullptr;
+        scratch_ptr[dev] = static_cast<uint32_t*>(ptr);
+    }
+    return scratch_ptr[dev];
+}
 
 size_t decode_layers_workspace_bytes() { return (size_t)decode::kWsWords * 4; }
 int64_t decode_layers_trace_words() { return decode::kTrWords; }

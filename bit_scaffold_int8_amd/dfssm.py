@@ -26,7 +26,7 @@ EXPORTED = ("dfssm_status_string", "dfssm_version", "dfssm_quantize_act", "dfssm
             "dfssm_scaffold_lora_forward_strided_batched", "dfssm_int8_rowscale_gemm",
             "dfssm_int8_rowscale_gemm_strided_batched", "dfssm_embedding_lookup", "dfssm_mamba2_decode_step",
             "dfssm_prefill_plan", "dfssm_decode_layers_workspace_bytes", "dfssm_decode_layers_trace_words",
-            "dfssm_decode_layers")
+            "dfssm_decode_layers", "dfssm_decode_layers_noalloc")
 
 DFSSM_DECODE_STATUS_TIMEOUT = 1
 DFSSM_DECODE_STATUS_GAVE_UP = 2
@@ -82,6 +82,7 @@ def _load():
         "dfssm_prefill_plan": [i64, i64, i64, i64, P, P, P],
         "dfssm_decode_layers": [P, i64, P, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t, P, P, i64, ctypes.c_uint32,
                                 P],
+        "dfssm_decode_layers_noalloc": [P, i64, P, P, P, P, P, ctypes.c_float, P, P, i64, ctypes.c_uint32, P],
     }
     for name, argtypes in sigs.items():
         f = getattr(lib, name)
@@ -293,5 +294,15 @@ def dfssm_decode_layers(weights: dict, n_layers, x_in, x_out, conv_state_in, con
     nbytes = workspace.numel() * workspace.element_size()
     _call("dfssm_decode_layers", ctypes.addressof(w), int(n_layers), _ptr(x_in), _ptr(x_out), _ptr(conv_state_in),
           _ptr(conv_state_out), _ptr(ssm_state), float(eps), _ptr(workspace), nbytes, _ptr(status), _ptr(trace),
+          int(spin_limit), int(flags), _stream(stream))
+
+
+def dfssm_decode_layers_noalloc(weights: dict, n_layers, x_in, x_out, conv_state_in, conv_state_out, ssm_state,
+                                eps, status, trace=None, spin_limit: int = 0, flags: int = 0, stream=None) -> None:
+    """dfssm_decode_layers with the library's own per-GPU array as the workspace: nothing
+    is allocated; calls that overlap on one GPU race."""
+    w = DecodeLayerWeights(*[_ptr(weights[name]) for name in DECODE_WEIGHT_FIELDS])
+    _call("dfssm_decode_layers_noalloc", ctypes.addressof(w), int(n_layers), _ptr(x_in), _ptr(x_out),
+          _ptr(conv_state_in), _ptr(conv_state_out), _ptr(ssm_state), float(eps), _ptr(status), _ptr(trace),
           int(spin_limit), int(flags), _stream(stream))
 

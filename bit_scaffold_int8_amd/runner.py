@@ -197,7 +197,7 @@ class DeviceDecodeStack:
         self.trace_words = dfssm.dfssm_decode_layers_trace_words()
 
     def new_trace(self):
-        return torch.empty((self.L, self.trace_words), dtype=torch.int32, device=self.ssm_state.device)
+        return torch.zeros((self.L, self.trace_words), dtype=torch.int32, device=self.ssm_state.device)
 
     def step(self, x_in, x_out, parity: int = 0, trace=None, spin_limit: int = 0, flags: int = 0, stream=None):
         """One token through every layer: windows[parity] -> windows[1 - parity]."""

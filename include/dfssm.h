@@ -389,6 +389,25 @@ dfssm_status dfssm_decode_layers(const dfssm_decode_layer_weights* w, int64_t n_
                                  float eps, void* workspace, size_t workspace_bytes, int32_t* status,
                                  uint32_t* trace, int64_t spin_limit, uint32_t flags, hipStream_t stream);
 
+/*
+ * dfssm_decode_layers for callers that cannot allocate device memory (code that must
+ * not call hipMalloc: tight serving loops, harnesses that forbid it).  Same arguments,
+ * results and errors, minus the workspace: the library's own array of
+ * dfssm_decode_layers_workspace_bytes() bytes per GPU (a file-scope device array, held
+ * until the process ends; its counters are cleared on `stream` the first time a device
+ * is used, and every call leaves them cleared) serves instead, so nothing is
+ * allocated or freed.  The array's size covers the largest stack the call accepts
+ * (n_layers <= 64; larger is DFSSM_ERR_INVALID_ARG).  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (other streams, other threads) race, so
+ * the caller serializes them (one stream does).  DFSSM_ERR_HIP if the array's device
+ * address cannot be obtained.
+ */
+dfssm_status dfssm_decode_layers_noalloc(const dfssm_decode_layer_weights* w, int64_t n_layers,
+                                         const float* x_in, float* x_out,
+                                         const float* conv_state_in, float* conv_state_out, float* ssm_state,
+                                         float eps, int32_t* status, uint32_t* trace, int64_t spin_limit,
+                                         uint32_t flags, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
