@@ -164,6 +164,7 @@ def parse():
     ap.add_argument("--prefill-iters", type=int, default=10)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMV traffic record from two rocprofv3 counter_collection.csv files")
+    ap.add_argument("--density-only", action="store_true", help="only the density-field codec leg")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the 48-layer decode legs (persistent one-launch and per-call chain)")
     ap.add_argument("--mamba2-only", action="store_true",
@@ -456,6 +457,39 @@ def decode_persistent_48l(torch, dev, tokens):
                     "and state prefetched while waiting"}
 
 
+def density_field_bench(torch, dev, iters):
+    """The density-field codec on one layer's SSM state for 64 sequences (64 x 64 heads x
+    64 channels = 262144 rows of 128 fp32 values, 128 MiB): encode, decode (the readout),
+    and the in-place round trip a chunk boundary applies.  Bytes per row: encode
+    512 read + 68 written; decode 68 read + 512 written; round trip 512 read + 512 + 68
+    written."""
+    from bit_scaffold_int8_amd import dfssm
+    R, d = 64 * 64 * 64, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(8)
+    x = 0.1 * torch.randn((R, d), device=dev, generator=g)
+    field = torch.empty((R, d // 8), dtype=torch.int32, device=dev)
+    scale = torch.empty((R,), dtype=torch.float32, device=dev)
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    work = x.clone()
+    legs = {
+        "encode": (lambda: dfssm.dfssm_density_field_encode(x, field, scale, stream), 580),
+        "decode": (lambda: dfssm.dfssm_density_field_decode(field, scale, out, stream), 580),
+        "requantize": (lambda: dfssm.dfssm_density_field_requantize(work, field, scale, stream), 1092),
+    }
+    res = {"rows": R, "d_state": d, "field_bytes_per_row": d // 8 * 4 + 4, "state_bytes_per_row": 4 * d}
+    for name, (fn, per_row) in legs.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ms = time_events(torch, fn, iters, stream)
+        res[name] = {"us": round(ms * 1e3, 2), "GBps": round(R * per_row / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(R * per_row / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del x, field, scale, out, work
+    return res
+
+
 def mfma_probe():
     """int8 MFMA rate this GPU sustains on given operand data (libdfssm_probe.so)."""
     import ctypes
@@ -569,6 +603,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    if args.density_only:
+        print(json.dumps({"density_field_codec": density_field_bench(torch, dev, 20)}))
+        return
     if args.decode_only:
         print(json.dumps({"decode_persistent_48l": decode_persistent_48l(torch, dev, 128),
                           "decode_chain_48l": decode_chain_48l(torch, dev, 64)}))
@@ -758,6 +795,8 @@ def main():
             progress("48-layer sweep")
         out["mamba2_decode_step"] = mamba2_step_bench(torch, dev, 20)
         progress("Mamba-2 step")
+        out["density_field_codec"] = density_field_bench(torch, dev, 20)
+        progress("density-field codec")
         if not args.no_sweeps:
             out["decode_chain_48l"] = decode_chain_48l(torch, dev, 64)    # 64 two-token replays
             progress("48-layer chain")

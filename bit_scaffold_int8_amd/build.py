@@ -13,7 +13,8 @@ LIB = os.path.join(PKG, "libdfssm.so")
 PROBE_LIB = os.path.join(PKG, "libdfssm_probe.so")
 PROBE_SOURCES = ["probe_mfma.hip"]
 SOURCES = ["api.hip", "quantize.hip", "lora_down.hip", "gemv.hip", "gemm_mfma.hip", "gemm_prefill.hip",
-           "int8_head.hip", "mamba2_step.hip", "decode_layers.hip"]
+           "int8_head.hip", "mamba2_step.hip", "decode_layers.hip",
+           "density_field.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -38,6 +38,11 @@ hipError_t launch_mamba2_step(const float* zxbcdt, int64_t S, int nheads, const 
                               float* ssm_state, const float* conv_w, const float* conv_b, const float* dt_bias,
                               const float* A_log, const float* D, const float* norm_w, float eps, float* out,
                               hipStream_t stream);
+bool density_field_supported(int64_t d_state);
+hipError_t launch_density_encode(const float* state, int64_t R, int64_t D, uint32_t* field, float* scale,
+                                 float* state_out, hipStream_t stream);
+hipError_t launch_density_decode(const uint32_t* field, const float* scale, int64_t R, int64_t D, float* state,
+                                 hipStream_t stream);
 size_t decode_layers_workspace_bytes();
 uint32_t* decode_layers_scratch(hipStream_t stream);
 int64_t decode_layers_trace_words();
@@ -259,6 +264,13 @@ dfssm_status decode_layers_impl(const dfssm_decode_layer_weights* w, int64_t n_l
     return e == hipSuccess ? DFSSM_OK : DFSSM_ERR_HIP;
 }
 
+dfssm_status density_checks(int64_t rows, int64_t d_state) {
+    if (rows <= 0 || d_state <= 0) return DFSSM_ERR_INVALID_ARG;
+    if (!dfssm::density_field_supported(d_state)) return DFSSM_ERR_UNSUPPORTED;
+    if (rows >= ((int64_t)1 << 40) / d_state) return DFSSM_ERR_INVALID_ARG;
+    return DFSSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -400,6 +412,35 @@ dfssm_status dfssm_embedding_lookup(const int32_t* tokens, int64_t T, const int8
     if (V * K >= ((int64_t)1 << 40) || T * K >= ((int64_t)1 << 40)) return DFSSM_ERR_UNSUPPORTED;
     return dfssm::launch_embedding_lookup(tokens, T, e, s_e, V, K, out, stream) == hipSuccess ? DFSSM_OK
                                                                                             : DFSSM_ERR_HIP;
+}
+
+dfssm_status dfssm_density_field_encode(const float* state, int64_t rows, int64_t d_state, uint32_t* field,
+                                        float* scale, hipStream_t stream) {
+    if (!state || !field || !scale) return DFSSM_ERR_INVALID_ARG;
+    if (dfssm_status st = density_checks(rows, d_state)) return st;
+    if (!aligned16(state) || !aligned16(field) || !aligned4(scale)) return DFSSM_ERR_INVALID_ARG;
+    return dfssm::launch_density_encode(state, rows, d_state, field, scale, nullptr, stream) == hipSuccess
+               ? DFSSM_OK
+               : DFSSM_ERR_HIP;
+}
+
+dfssm_status dfssm_density_field_decode(const uint32_t* field, const float* scale, int64_t rows, int64_t d_state,
+                                        float* state, hipStream_t stream) {
+    if (!state || !field || !scale) return DFSSM_ERR_INVALID_ARG;
+    if (dfssm_status st = density_checks(rows, d_state)) return st;
+    if (!aligned16(state) || !aligned4(field) || !aligned4(scale)) return DFSSM_ERR_INVALID_ARG;
+    return dfssm::launch_density_decode(field, scale, rows, d_state, state, stream) == hipSuccess ? DFSSM_OK
+                                                                                                 : DFSSM_ERR_HIP;
+}
+
+dfssm_status dfssm_density_field_requantize(float* state, int64_t rows, int64_t d_state, uint32_t* field,
+                                            float* scale, hipStream_t stream) {
+    if (!state) return DFSSM_ERR_INVALID_ARG;
+    if (dfssm_status st = density_checks(rows, d_state)) return st;
+    if (!aligned16(state) || !aligned4_or_null(field) || !aligned4_or_null(scale)) return DFSSM_ERR_INVALID_ARG;
+    return dfssm::launch_density_encode(state, rows, d_state, field, scale, state, stream) == hipSuccess
+               ? DFSSM_OK
+               : DFSSM_ERR_HIP;
 }
 
 size_t dfssm_decode_layers_workspace_bytes(void) { return dfssm::decode_layers_workspace_bytes(); }

@@ -1,0 +1,165 @@
+// density_field.hip -- the density-field state codec (gfx950).
+//
+// DF-SSM technical summary (gist.science), section 2D "Density Field State
+// Representation": the SSM state is held as a binary field per state element, with
+// about 4 d_state cells, through normalization, sigma-delta injection (error feedback),
+// binarization and a popcount readout, at chunk boundaries.  Here a state element is
+// one row of d_state values (one channel of one head), and:
+//   s     = max_n |v_n|                               (the row's scale, fp32)
+//   u_n   = (v_n / s + 1) / 2                          (density in [0, 1]; 1/2 if s = 0)
+//   cells: a first-order modulator over the row's 4 d_state cells in order, value n
+//          owning cells 4 n .. 4 n + 3: w = u_n + e; cell = (w >= 1/2); e = w - cell
+//   v'_n  = s (2 popcount(cells of n) / 4 - 1)          (readout: s times -1 .. 1 in halves)
+// Storage: 32 cells per uint32 (cell c in bit c % 32 of word c / 32: value n is nibble
+// n % 8 of word n / 8), d_state / 8 words and one fp32 scale per row -- 68 bytes for a
+// 512-byte row of 128 fp32 values.
+//
+// The modulator is a chain over a row's cells, so a thread takes a whole row: a group
+// of 64 threads stages 64 rows through LDS with coalesced 16-byte loads (row stride
+// d_state + 1 words, so the threads' reads of their own rows fall in distinct banks),
+// then each thread runs its row's chain in registers and writes its words.  The
+// readout is one thread per word (eight popcounts, two 16-byte stores).  Both passes
+// are bound by HBM traffic (the state) at the sizes a decode batch holds.
+#include "device_common.h"
+
+namespace dfssm {
+
+namespace {
+
+constexpr int kDfRows = 64;       // rows per encode group, one per thread
+constexpr int kDfDecThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kDfRows) void density_encode_kernel(const float* __restrict__ state, int64_t R,
+                                                                  uint32_t* __restrict__ field,
+                                                                  float* __restrict__ scale,
+                                                                  float* __restrict__ state_out) {
+    constexpr int LD = D + 1;
+    constexpr int W = D / 8;  // words per row
+    __shared__ float tile[kDfRows * LD];
+    const int64_t r0 = (int64_t)blockIdx.x * kDfRows;
+    const int rows = (int)(R - r0 < kDfRows ? R - r0 : kDfRows);
+    const int tid = threadIdx.x;
+
+    // the group's rows, coalesced: consecutive threads load consecutive 16-byte pieces
+    const float4* src = reinterpret_cast<const float4*>(state + r0 * D);
+    for (int i = tid; i < rows * (D / 4); i += kDfRows) {
+        const float4 v = src[i];
+        float* dst = tile + (i / (D / 4)) * LD + (i % (D / 4)) * 4;
+        dst[0] = v.x;
+        dst[1] = v.y;
+        dst[2] = v.z;
+        dst[3] = v.w;
+    }
+    __syncthreads();
+
+    if (tid < rows) {
+        float* const row = tile + tid * LD;
+        float s = 0.0f;
+#pragma unroll 8
+        for (int n = 0; n < D; ++n) s = fmaxf(s, fabsf(row[n]));
+        const int64_t r = r0 + tid;
+        float e = 0.0f;
+        // one word (8 values, 32 cells) per trip; its values are read before the
+        // round trip overwrites them with the readout
+#pragma unroll 1
+        for (int w = 0; w < W; ++w) {
+            uint32_t bits = 0u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float a = s > 0.0f ? row[8 * w + j] / s : 0.0f;  // IEEE division
+                const float u = (a + 1.0f) * 0.5f;                      // the halving is exact
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float wv = u + e;            // inject the carried error
+                    const bool b = wv >= 0.5f;         // binarize
+                    e = b ? wv - 1.0f : wv;            // the residual (exact)
+                    bits |= (uint32_t)b << (4 * j + k);
+                }
+            }
+            if (field) field[r * W + w] = bits;
+            if (state_out) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int pc = __builtin_popcount((bits >> (4 * j)) & 0xFu);
+                    row[8 * w + j] = s * ((float)pc * 0.5f - 1.0f);
+                }
+            }
+        }
+        if (scale) scale[r] = s;
+    }
+    if (state_out) {
+        __syncthreads();
+        float4* dst = reinterpret_cast<float4*>(state_out + r0 * D);
+        for (int i = tid; i < rows * (D / 4); i += kDfRows) {
+            const float* p = tile + (i / (D / 4)) * LD + (i % (D / 4)) * 4;
+            dst[i] = make_float4(p[0], p[1], p[2], p[3]);
+        }
+    }
+}
+
+// One thread per field word: its eight values.
+template <int D>
+__global__ __launch_bounds__(kDfDecThreads) void density_decode_kernel(const uint32_t* __restrict__ field,
+                                                                        const float* __restrict__ scale, int64_t R,
+                                                                        float* __restrict__ state) {
+    constexpr int W = D / 8;
+    const int64_t i = (int64_t)blockIdx.x * kDfDecThreads + threadIdx.x;
+    if (i >= R * W) return;
+    const uint32_t w = field[i];
+    const float s = scale[i / W];
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int pc = __builtin_popcount((w >> (4 * j)) & 0xFu);
+        v[j] = s * ((float)pc * 0.5f - 1.0f);
+    }
+    float4* dst = reinterpret_cast<float4*>(state + i * 8);
+    dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+    dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+template <int D>
+hipError_t launch_encode_d(const float* state, int64_t R, uint32_t* field, float* scale, float* state_out,
+                           hipStream_t stream) {
+    const int64_t groups = (R + kDfRows - 1) / kDfRows;
+    if (groups > 0x7fffffffLL) return hipErrorInvalidValue;
+    density_encode_kernel<D><<<dim3((unsigned)groups), kDfRows, 0, stream>>>(state, R, field, scale, state_out);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(const uint32_t* field, const float* scale, int64_t R, float* state, hipStream_t stream) {
+    const int64_t groups = (R * (D / 8) + kDfDecThreads - 1) / kDfDecThreads;
+    if (groups > 0x7fffffffLL) return hipErrorInvalidValue;
+    density_decode_kernel<D><<<dim3((unsigned)groups), kDfDecThreads, 0, stream>>>(field, scale, R, state);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool density_field_supported(int64_t d_state) { return d_state == 64 || d_state == 128 || d_state == 256; }
+
+// encode (state_out == NULL) or the in-place round trip (state_out == state; field and
+// scale optional)
+hipError_t launch_density_encode(const float* state, int64_t R, int64_t D, uint32_t* field, float* scale,
+                                 float* state_out, hipStream_t stream) {
+    switch (D) {
+        case 64: return launch_encode_d<64>(state, R, field, scale, state_out, stream);
+        case 128: return launch_encode_d<128>(state, R, field, scale, state_out, stream);
+        case 256: return launch_encode_d<256>(state, R, field, scale, state_out, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_density_decode(const uint32_t* field, const float* scale, int64_t R, int64_t D, float* state,
+                                 hipStream_t stream) {
+    switch (D) {
+        case 64: return launch_decode_d<64>(field, scale, R, state, stream);
+        case 128: return launch_decode_d<128>(field, scale, R, state, stream);
+        case 256: return launch_decode_d<256>(field, scale, R, state, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dfssm

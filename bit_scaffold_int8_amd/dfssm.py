@@ -26,7 +26,8 @@ EXPORTED = ("dfssm_status_string", "dfssm_version", "dfssm_quantize_act", "dfssm
             "dfssm_scaffold_lora_forward_strided_batched", "dfssm_int8_rowscale_gemm",
             "dfssm_int8_rowscale_gemm_strided_batched", "dfssm_embedding_lookup", "dfssm_mamba2_decode_step",
             "dfssm_prefill_plan", "dfssm_decode_layers_workspace_bytes", "dfssm_decode_layers_trace_words",
-            "dfssm_decode_layers", "dfssm_decode_layers_noalloc")
+            "dfssm_decode_layers", "dfssm_decode_layers_noalloc", "dfssm_density_field_encode",
+            "dfssm_density_field_decode", "dfssm_density_field_requantize")
 
 DFSSM_DECODE_STATUS_TIMEOUT = 1
 DFSSM_DECODE_STATUS_GAVE_UP = 2
@@ -83,6 +84,9 @@ def _load():
         "dfssm_decode_layers": [P, i64, P, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t, P, P, i64, ctypes.c_uint32,
                                 P],
         "dfssm_decode_layers_noalloc": [P, i64, P, P, P, P, P, ctypes.c_float, P, P, i64, ctypes.c_uint32, P],
+        "dfssm_density_field_encode": [P, i64, i64, P, P, P],
+        "dfssm_density_field_decode": [P, P, i64, i64, P, P],
+        "dfssm_density_field_requantize": [P, i64, i64, P, P, P],
     }
     for name, argtypes in sigs.items():
         f = getattr(lib, name)
@@ -305,4 +309,22 @@ def dfssm_decode_layers_noalloc(weights: dict, n_layers, x_in, x_out, conv_state
     _call("dfssm_decode_layers_noalloc", ctypes.addressof(w), int(n_layers), _ptr(x_in), _ptr(x_out),
           _ptr(conv_state_in), _ptr(conv_state_out), _ptr(ssm_state), float(eps), _ptr(status), _ptr(trace),
           int(spin_limit), int(flags), _stream(stream))
+
+
+def dfssm_density_field_encode(state, field, scale, stream=None) -> None:
+    """state fp32 [R, d] -> field uint32 [R, d / 8], scale fp32 [R] (density-field codec)."""
+    R, d = state.shape
+    _call("dfssm_density_field_encode", _ptr(state), R, d, _ptr(field), _ptr(scale), _stream(stream))
+
+
+def dfssm_density_field_decode(field, scale, state, stream=None) -> None:
+    """field uint32 [R, d / 8], scale fp32 [R] -> state fp32 [R, d] (popcount readout)."""
+    R, d = state.shape
+    _call("dfssm_density_field_decode", _ptr(field), _ptr(scale), R, d, _ptr(state), _stream(stream))
+
+
+def dfssm_density_field_requantize(state, field=None, scale=None, stream=None) -> None:
+    """The round trip in place: state [R, d] <- its field's readout (field, scale optional)."""
+    R, d = state.shape
+    _call("dfssm_density_field_requantize", _ptr(state), R, d, _ptr(field), _ptr(scale), _stream(stream))
 

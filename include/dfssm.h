@@ -408,6 +408,37 @@ dfssm_status dfssm_decode_layers_noalloc(const dfssm_decode_layer_weights* w, in
                                          float eps, int32_t* status, uint32_t* trace, int64_t spin_limit,
                                          uint32_t flags, hipStream_t stream);
 
+/*
+ * The density-field state codec (technical summary section 2D, "Density Field State
+ * Representation": a binary field of about 4 d_state cells per state element, through
+ * normalization, sigma-delta injection with error feedback, binarization and a
+ * popcount readout, applied at chunk boundaries).  A state element is one row of
+ * d_state fp32 values (one channel of one head of the SSM state, e.g. [S][64][64][128]
+ * is 4096 S rows of 128).  Per row, with value n owning cells 4n .. 4n + 3:
+ *   s   = max_n |v_n|                       (scale, fp32)
+ *   u_n = (v_n / s + 1) / 2                 (IEEE division; 1/2 when s = 0)
+ *   cells in order, e = 0 at the row's start: w = u_n + e; cell = (w >= 1/2); e = w - cell
+ *   readout v'_n = s * (popcount(cells of n) * 0.5 - 1)   (s times -1, -1/2, 0, 1/2 or 1)
+ * Field layout: uint32 [rows][d_state / 8]; cell c is bit c % 32 of word c / 32, so value
+ * n is nibble n % 8 of word n / 8 (the notional K x K field, K = ceil(sqrt(4 d_state)),
+ * keeps its remaining K^2 - 4 d_state cells at 0; they are not stored).
+ *   state  fp32 [rows][d_state] (16-byte aligned)
+ *   field  uint32 [rows][d_state / 8] (16-byte aligned)   scale fp32 [rows]
+ * d_state must be 64, 128 or 256 (DFSSM_ERR_UNSUPPORTED otherwise); rows >= 1 and
+ * rows * d_state < 2^40.  Non-finite state values are a precondition violation.
+ *   encode:      state -> field, scale
+ *   decode:      field, scale -> state (the readout)
+ *   requantize:  the round trip at a chunk boundary, in place: state <- readout of its
+ *                own field; field and scale are also written when not NULL
+ * One kernel launch each on `stream`; nothing is allocated.
+ */
+dfssm_status dfssm_density_field_encode(const float* state, int64_t rows, int64_t d_state, uint32_t* field,
+                                        float* scale, hipStream_t stream);
+dfssm_status dfssm_density_field_decode(const uint32_t* field, const float* scale, int64_t rows, int64_t d_state,
+                                        float* state, hipStream_t stream);
+dfssm_status dfssm_density_field_requantize(float* state, int64_t rows, int64_t d_state, uint32_t* field,
+                                            float* scale, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -280,3 +280,51 @@ def test_prefill_plan_rejects():
             dfssm.dfssm_prefill_plan(*args)
         assert e.value.status == want, args
     assert dfssm.lib.dfssm_prefill_plan(2048, 512, 2048, 1, None, None, None) == I
+
+
+# ---- the density-field codec and the one-launch decode (host-side checks only)
+
+@pytest.mark.parametrize("args,want", [
+    ((None, 10, 128, A, A), 1), ((A, 10, 128, None, A), 1), ((A, 10, 128, A, None), 1),
+    ((A, 0, 128, A, A), 1), ((A, 10, 0, A, A), 1), ((A, 10, 100, A, A), 2), ((A, 10, 512, A, A), 2),
+    ((A + 4, 10, 128, A, A), 1), ((A, 10, 128, A + 8, A), 1), ((A, 10, 128, A, A + 2), 1),
+    ((A, 1 << 34, 128, A, A), 1),
+])
+def test_density_encode_rejects(args, want):
+    assert _raw("dfssm_density_field_encode", *args, None) == want
+
+
+def test_density_decode_and_requantize_reject():
+    assert _raw("dfssm_density_field_decode", None, A, 10, 128, A, None) == 1
+    assert _raw("dfssm_density_field_decode", A, A, 10, 96, A, None) == 2
+    assert _raw("dfssm_density_field_decode", A, A, 10, 128, A + 4, None) == 1
+    assert _raw("dfssm_density_field_requantize", None, 10, 128, None, None, None) == 1
+    assert _raw("dfssm_density_field_requantize", A, 10, 32, None, None, None) == 2
+    assert _raw("dfssm_density_field_requantize", A + 8, 10, 128, None, None, None) == 1
+
+
+def _decode_layers(**kw):
+    import ctypes
+    from bit_scaffold_int8_amd import dfssm
+    far = 0x10000000
+    fields = {name: A for name in dfssm.DECODE_WEIGHT_FIELDS}
+    fields.update(kw.pop("weights", {}))
+    w = dfssm.DecodeLayerWeights(*[fields[n] for n in dfssm.DECODE_WEIGHT_FIELDS])
+    a = dict(L=2, x_in=A, x_out=A, conv_in=A, conv_out=A + far, ssm=A, eps=1e-5, ws=A,
+             ws_bytes=dfssm.dfssm_decode_layers_workspace_bytes(), status=A, trace=None, spin=0, flags=0)
+    a.update(kw)
+    return dfssm.raw("dfssm_decode_layers", None if a.get("null_w") else ctypes.addressof(w), a["L"], a["x_in"],
+                     a["x_out"], a["conv_in"], a["conv_out"], a["ssm"], a["eps"], a["ws"], a["ws_bytes"], a["status"],
+                     a["trace"], a["spin"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(null_w=True), 1), (dict(weights={"in_w_bits": None}), 1), (dict(weights={"norm_w": A + 4}), 1),
+    (dict(weights={"out_s_b": A + 2}), 1), (dict(L=0), 1), (dict(L=65), 1), (dict(x_in=None), 1),
+    (dict(x_in=A + 4), 1), (dict(ssm=None), 1), (dict(ssm=A + 8), 1), (dict(ws=None), 1), (dict(ws=A + 8), 1),
+    (dict(ws_bytes=64), 1), (dict(status=None), 1), (dict(status=A + 1), 1), (dict(trace=A + 2), 1),
+    (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1), (dict(flags=2), 1),
+    (dict(conv_out=A), 1), (dict(conv_out=A + 4352 * 16), 1),       # the windows overlap (2 layers)
+])
+def test_decode_layers_rejects(kw, want):
+    assert _decode_layers(**kw) == want
