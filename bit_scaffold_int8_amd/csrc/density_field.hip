@@ -14,10 +14,12 @@
 // n % 8 of word n / 8), d_state / 8 words and one fp32 scale per row -- 68 bytes for a
 // 512-byte row of 128 fp32 values.
 //
-// The modulator is a chain over a row's cells, so a thread takes a whole row: a group
-// of 64 threads stages 64 rows through LDS with coalesced 16-byte loads (row stride
-// d_state + 1 words, so the threads' reads of their own rows fall in distinct banks),
-// then each thread runs its row's chain in registers and writes its words.  The
+// The modulator is a chain over a row's cells, so a thread takes a whole row, held in
+// registers: a group of 64 threads stages its 64 rows through LDS 32 values at a time
+// with coalesced 16-byte loads (chunk stride 33 words, so each thread's copy of its own
+// row falls in distinct banks), computes the densities (independent divisions, ahead
+// of the chain), then runs the chain and writes its words.  A small tile keeps several
+// groups resident per SIMD, so their chains overlap.  The
 // readout is one thread per word (eight popcounts, two 16-byte stores).  Both passes
 // are bound by HBM traffic (the state) at the sizes a decode batch holds.
 #include "device_common.h"
@@ -34,66 +36,110 @@ __global__ __launch_bounds__(kDfRows) void density_encode_kernel(const float* __
                                                                   uint32_t* __restrict__ field,
                                                                   float* __restrict__ scale,
                                                                   float* __restrict__ state_out) {
-    constexpr int LD = D + 1;
-    constexpr int W = D / 8;  // words per row
+    constexpr int W = D / 8;                 // field words per row
+    constexpr int kChunk = 32;               // values per staged chunk of the group's rows
+    constexpr int LD = kChunk + 1;           // LDS row stride of a chunk (words)
     __shared__ float tile[kDfRows * LD];
     const int64_t r0 = (int64_t)blockIdx.x * kDfRows;
     const int rows = (int)(R - r0 < kDfRows ? R - r0 : kDfRows);
     const int tid = threadIdx.x;
 
-    // the group's rows, coalesced: consecutive threads load consecutive 16-byte pieces
-    const float4* src = reinterpret_cast<const float4*>(state + r0 * D);
-    for (int i = tid; i < rows * (D / 4); i += kDfRows) {
-        const float4 v = src[i];
-        float* dst = tile + (i / (D / 4)) * LD + (i % (D / 4)) * 4;
-        dst[0] = v.x;
-        dst[1] = v.y;
-        dst[2] = v.z;
-        dst[3] = v.w;
+    // the thread's row in registers, chunk by chunk: coalesced 16-byte loads of the
+    // group's rows into LDS (eight threads per 128-byte piece of a row), then each
+    // thread copies its own row's chunk out (stride 33: distinct banks)
+    // every load of the group's tile is issued first (their registers then become the
+    // row's values chunk by chunk, so the peak stays near one row per thread)
+    float4 raw[D / kChunk][kChunk / 4];
+#pragma unroll
+    for (int q = 0; q < D / kChunk; ++q) {
+#pragma unroll
+        for (int i = 0; i < kChunk / 4; ++i) {
+            const int idx = tid + kDfRows * i;               // float4 piece of the chunk
+            const int row = idx / (kChunk / 4), c4 = idx % (kChunk / 4);
+            raw[q][i] = row < rows ? *reinterpret_cast<const float4*>(state + (r0 + row) * D + kChunk * q + 4 * c4)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
-    __syncthreads();
+    float v[D];
+#pragma unroll
+    for (int q = 0; q < D / kChunk; ++q) {
+#pragma unroll
+        for (int i = 0; i < kChunk / 4; ++i) {
+            const int idx = tid + kDfRows * i;
+            const int row = idx / (kChunk / 4), c4 = idx % (kChunk / 4);
+            float* dst = tile + row * LD + 4 * c4;
+            dst[0] = raw[q][i].x;
+            dst[1] = raw[q][i].y;
+            dst[2] = raw[q][i].z;
+            dst[3] = raw[q][i].w;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) v[kChunk * q + c] = tile[tid * LD + c];
+        __syncthreads();
+    }
 
-    if (tid < rows) {
-        float* const row = tile + tid * LD;
-        float s = 0.0f;
-#pragma unroll 8
-        for (int n = 0; n < D; ++n) s = fmaxf(s, fabsf(row[n]));
-        const int64_t r = r0 + tid;
-        float e = 0.0f;
-        // one word (8 values, 32 cells) per trip; its values are read before the
-        // round trip overwrites them with the readout
-#pragma unroll 1
-        for (int w = 0; w < W; ++w) {
-            uint32_t bits = 0u;
+    const bool live = tid < rows;
+    float s = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float a = s > 0.0f ? row[8 * w + j] / s : 0.0f;  // IEEE division
-                const float u = (a + 1.0f) * 0.5f;                      // the halving is exact
+    for (int n = 0; n < D; ++n) s = fmaxf(s, fabsf(v[n]));
+    // densities, in place: independent divisions, ahead of the chain
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float wv = u + e;            // inject the carried error
-                    const bool b = wv >= 0.5f;         // binarize
-                    e = b ? wv - 1.0f : wv;            // the residual (exact)
-                    bits |= (uint32_t)b << (4 * j + k);
-                }
+    for (int n = 0; n < D; ++n) {
+        const float a = s > 0.0f ? v[n] / s : 0.0f;  // IEEE division
+        v[n] = (a + 1.0f) * 0.5f;                    // the halving is exact
+    }
+    // the modulator over the row's cells, 32 cells (8 values) per field word
+    const int64_t r = r0 + (live ? tid : 0);
+    float e = 0.0f;
+    uint32_t words[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float u = v[8 * w + j];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float wv = u + e;            // inject the carried error
+                const bool b = wv >= 0.5f;         // binarize
+                e = b ? wv - 1.0f : wv;            // the residual (exact)
+                bits |= (uint32_t)b << (4 * j + k);
             }
-            if (field) field[r * W + w] = bits;
-            if (state_out) {
+        }
+        words[w] = bits;
+    }
+    if (live) {
+        if (field) {
+            uint4* dst = reinterpret_cast<uint4*>(field + r * W);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int pc = __builtin_popcount((bits >> (4 * j)) & 0xFu);
-                    row[8 * w + j] = s * ((float)pc * 0.5f - 1.0f);
-                }
-            }
+            for (int q = 0; q < W / 4; ++q)
+                dst[q] = make_uint4(words[4 * q], words[4 * q + 1], words[4 * q + 2], words[4 * q + 3]);
         }
         if (scale) scale[r] = s;
     }
     if (state_out) {
-        __syncthreads();
-        float4* dst = reinterpret_cast<float4*>(state_out + r0 * D);
-        for (int i = tid; i < rows * (D / 4); i += kDfRows) {
-            const float* p = tile + (i / (D / 4)) * LD + (i % (D / 4)) * 4;
-            dst[i] = make_float4(p[0], p[1], p[2], p[3]);
+        // the readout, written back through the same chunked transposition
+#pragma unroll
+        for (int q = 0; q < D / kChunk; ++q) {
+#pragma unroll
+            for (int c = 0; c < kChunk; ++c) {
+                const int n = kChunk * q + c;
+                const int pc = __builtin_popcount((words[n >> 3] >> (4 * (n & 7))) & 0xFu);
+                tile[tid * LD + c] = s * ((float)pc * 0.5f - 1.0f);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kChunk / 4; ++i) {
+                const int idx = tid + kDfRows * i;
+                const int row = idx / (kChunk / 4), c4 = idx % (kChunk / 4);
+                if (row < rows) {
+                    const float* p = tile + row * LD + 4 * c4;
+                    *reinterpret_cast<float4*>(state_out + (r0 + row) * D + kChunk * q + 4 * c4) =
+                        make_float4(p[0], p[1], p[2], p[3]);
+                }
+            }
+            __syncthreads();
         }
     }
 }
