@@ -22,6 +22,11 @@
 //  * K is split across the workgroup's waves (16-byte chunks, 4 lane groups per
 //    wave); the per-wave partial tiles are summed through LDS, then the fused
 //    epilogue applies s_w, the LoRA up-projection and s_x and writes fp32 y.
+//  * Epilogue operands: the group's rows of W_A, s_A and s_w are copied into LDS at the
+//    start by buffer loads with an LDS destination (no registers held).  For up to 4
+//    tokens, the LoRA up-projection of every row is formed once after the setup and y
+//    is held in LDS, written after the last stage: small scattered stores interleaved
+//    with the packed-sign stream slow the stream far beyond their bytes.
 //  * Memory pipeline: rows go in stages of T 16-row tiles.  Packed-sign loads are
 //    16 bytes per lane (64-byte runs per row per instruction), issued two stages
 //    ahead of their use from clamped always-valid addresses (never masked, so never
@@ -73,6 +78,9 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
     int64_t num_tiles, int stages_per_wg, FusedIO fio) {
     constexpr bool kFused = kSetup == kQuantize;
     static_assert(!kFused || (kFast && C == 1), "the fused setup needs whole 128-k chunks, one per lane");
+    constexpr int kSubThreads = W * kWave;
+    const int tid = (int)threadIdx.x;
+    const int64_t prob = blockIdx.y;
     // epilogue: thread -> one row of the stage (its W_A row, s_A, s_w are loaded once per
     // stage) and E of that row's tokens
     static_assert((W * kWave) % (T * 16) == 0, "a stage's rows must divide the group size");
@@ -101,9 +109,9 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
     __shared__ float amax_part[kFused ? W : 1][4];
     __shared__ int32_t tsum[kSetup != kGivenT ? 16 : 1][kRank];
 
-    // problem blockIdx.y of a dense batch (every operand advanced by its own size)
+    // problem `prob` of a dense batch (every operand advanced by its own size)
     {
-        const int64_t p = blockIdx.y;
+        const int64_t p = prob;
         x_q += p * M * K;
         s_x += p * M;
         w_bits += p * N * (K / 8);
@@ -118,8 +126,8 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         }
     }
 
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
     const int i = lane & 15;
     const int g = lane >> 4;
     const int64_t RB = K / 8;
@@ -176,43 +184,30 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         prefetch(st_begin + 1 < st_end ? st_begin + 1 : st_end - 1, s1);
     };
 
-    // The group's rows: W_A row, s_A and s_w go to LDS (rank 0: zero LoRA operands).
-    // Loads complete in issue order, so anything issued ahead of the inputs the setup
-    // waits on would sit on its critical path: the setup issues its inputs first, then
-    // this thread's first row of epilogue operands (into registers) and the first two
-    // stages, and copies the operands to LDS only once its own work is done.
+    // The group's rows: W_A row, s_A and s_w go straight into LDS -- buffer loads with an
+    // LDS destination, so they hold no registers and nothing waits for them until the
+    // first stage's epilogue.  They are issued ahead of the first stages' signs: loads
+    // complete in issue order, so a wave that has its first stage's signs has its rows
+    // in LDS too, and that stage's barrier makes every wave's rows visible.  Lane l of a
+    // wave's load lands at the wave's LDS address + l times the size; slots past the
+    // group's rows (short of the next multiple of 64, inside the arrays) take clamped
+    // rows.  Rank 0 gives the LoRA operands an empty range: they read zero.
     const int64_t row0 = st_begin * T * 16;
     const int nrows = (int)((st_end - st_begin) * T * 16);
-    auto row_clamped = [&](int r) __attribute__((always_inline)) {
-        const int64_t n = row0 + r;
-        return n < N ? n : N - 1;
-    };
-    // (branch-free buffer loads: a load inside a branch makes the compiler copy its
-    // result at the join, which waits for every load issued before it; rank 0 gives
-    // the LoRA operands an empty range, so they read zero)
     const __amdgpu_buffer_rsrc_t sw_rsrc = make_rsrc(s_w, (uint32_t)(N * 4));
     const __amdgpu_buffer_rsrc_t wa_rsrc = make_rsrc(w_a, rank != 0 ? (uint32_t)(N * kRank) : 0u);
     const __amdgpu_buffer_rsrc_t sa_rsrc = make_rsrc(s_a, rank != 0 ? (uint32_t)(N * 4) : 0u);
-    float r0_sw, r0_sa;
-    uint4 r0_wa;
-    auto load_first_row = [&]() __attribute__((always_inline)) {
-        const int nc = (int)row_clamped((int)threadIdx.x < nrows ? (int)threadIdx.x : nrows - 1);
-        r0_sw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sw_rsrc, 4 * nc, 0, 0));
-        r0_sa = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sa_rsrc, 4 * nc, 0, 0));
-        const v4i wa = __builtin_amdgcn_raw_buffer_load_b128(wa_rsrc, kRank * nc, 0, 0);
-        r0_wa = make_uint4((uint32_t)wa[0], (uint32_t)wa[1], (uint32_t)wa[2], (uint32_t)wa[3]);
-    };
-    auto store_rows = [&]() __attribute__((always_inline)) {
-        if ((int)threadIdx.x < nrows) {
-            sw_lds[threadIdx.x] = r0_sw;
-            wa_lds[threadIdx.x] = r0_wa;
-            sa_lds[threadIdx.x] = r0_sa;
-        }
-        for (int r = threadIdx.x + W * kWave; r < nrows; r += W * kWave) {
-            const int64_t nc = row_clamped(r);
-            sw_lds[r] = s_w[nc];
-            wa_lds[r] = rank != 0 ? *reinterpret_cast<const uint4*>(w_a + nc * kRank) : make_uint4(0u, 0u, 0u, 0u);
-            sa_lds[r] = rank != 0 ? s_a[nc] : 0.0f;
+    auto issue_rows = [&]() __attribute__((always_inline)) {
+        const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+        for (int rw = wv * kWave; rw < nrows; rw += kSubThreads) {  // uniform per wave
+            const int64_t n = row0 + rw + lane;
+            const int nc = (int)(n < N ? n : N - 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wa_rsrc, (__attribute__((address_space(3))) void*)&wa_lds[rw],
+                                                     16, kRank * nc, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(sw_rsrc, (__attribute__((address_space(3))) void*)&sw_lds[rw],
+                                                     4, 4 * nc, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(sa_rsrc, (__attribute__((address_space(3))) void*)&sa_lds[rw],
+                                                     4, 4 * nc, 0, 0, 0);
         }
     };
 
@@ -224,11 +219,11 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         // MFMA tile whose rows are W_B's ranks.
         constexpr int NT = W * kWave;
         constexpr int kXV = kFusedMK / 4 / NT;  // float4 of the rows per thread (4)
-        const int64_t p = blockIdx.y;
+        const int64_t p = prob;
         const bool writer = blockIdx.x == 0;
         const int64_t MK4 = (int64_t)M * K / 4;
-        for (int e = threadIdx.x; e < 16 * kRank; e += NT) (&tsum[0][0])[e] = 0;
-        for (int e = threadIdx.x; e < 2 * T * 16 * 20; e += NT) (&red[0][0][0])[e] = 0;
+        for (int e = tid; e < 16 * kRank; e += NT) (&tsum[0][0])[e] = 0;
+        for (int e = tid; e < 2 * T * 16 * 20; e += NT) (&red[0][0][0])[e] = 0;
 
         // loads: the rows (float4 f = e NT + tid of the dense [M][K] block), this lane's
         // 128-k chunk of W_B row i as eight 16-byte pieces, and s_B
@@ -237,7 +232,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
 #pragma unroll
         for (int e = 0; e < kXV; ++e) {
             const v4f v = __builtin_bit_cast(
-                v4f, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (e * NT + (int)threadIdx.x) * 16, 0, 0));
+                v4f, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (e * NT + tid) * 16, 0, 0));
             xv[e] = make_float4(v[0], v[1], v[2], v[3]);
         }
         const int qch = wave * 4 + g;            // this lane's chunk (C == 1)
@@ -253,10 +248,10 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         float sbv[U];
 #pragma unroll
         for (int q = 0; q < U; ++q) {
-            const int e = threadIdx.x + q * NT;
+            const int e = tid + q * NT;
             sbv[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sb_rsrc, 4 * (e % kRank), 0, 0));
         }
-        load_first_row();
+        issue_rows();
         prefetch_first_stages();
         // every load above is issued before any of the work below waits on one
         __builtin_amdgcn_sched_barrier(0);
@@ -266,7 +261,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         // the values are zero, so any token will do.
         const int K32 = (int)K;
         auto token_of = [&](int e) __attribute__((always_inline)) {
-            const int k4 = 4 * (e * NT + (int)threadIdx.x);
+            const int k4 = 4 * (e * NT + tid);
             return (k4 >= K32 ? 1 : 0) + (k4 >= 2 * K32 ? 1 : 0) + (k4 >= 3 * K32 ? 1 : 0);
         };
         float am[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -305,7 +300,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         const __amdgpu_buffer_rsrc_t xq_rsrc = make_rsrc(fio.x_q + p * M * K, writer ? (uint32_t)(M * K) : 0u);
 #pragma unroll
         for (int e = 0; e < kXV; ++e) {
-            const int f = e * NT + (int)threadIdx.x;
+            const int f = e * NT + tid;
             const int m = token_of(e);
             float a = amx[0], s = sc[0], iv = inv[0];
             bool fs = fast[0];
@@ -319,13 +314,13 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
             if (f < MK4) codes_lds[f] = q;
             __builtin_amdgcn_raw_buffer_store_b32(q, xq_rsrc, f < MK4 ? 4 * f : kOffDead, 0, 0);
         }
-        if (threadIdx.x < 16) {
+        if (tid < 16) {
             float s = 0.0f;
 #pragma unroll
             for (int mm = 0; mm < 4; ++mm)
-                if ((int)threadIdx.x == mm && mm < M) s = sc[mm];
-            sxs[threadIdx.x] = s;
-            if (writer && (int)threadIdx.x < M) fio.s_x[p * M + threadIdx.x] = s;
+                if (tid == mm && mm < M) s = sc[mm];
+            sxs[tid] = s;
+            if (writer && tid < M) fio.s_x[p * M + tid] = s;
         }
         lds_barrier();
 
@@ -371,7 +366,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         lds_barrier();
 #pragma unroll
         for (int q = 0; q < U; ++q) {
-            const int e = threadIdx.x + q * NT;
+            const int e = tid + q * NT;
             if (e < 16 * kRank) {
                 const int tok = e / kRank, r = e % kRank;
                 const int32_t tt = tsum[tok][r];
@@ -379,18 +374,17 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
                 if (writer && rank != 0 && tok < M) fio.t[(p * M + tok) * kRank + r] = tt;
             }
         }
-        if (threadIdx.x < 16) {
+        if (tid < 16) {
             int32_t s = 0;
             for (int w = 0; w < W; ++w)
-                for (int gg = 0; gg < 4; ++gg) s += xs_part[w][16 * gg + threadIdx.x];
-            xsum[threadIdx.x] = s;
+                for (int gg = 0; gg < 4; ++gg) s += xs_part[w][16 * gg + tid];
+            xsum[tid] = s;
         }
-        store_rows();
-        // (u, xsum and the row operands are read after the first stage's barrier below)
+        // (u and xsum are read after the first stage's barrier below)
     } else {
         // kCodes: t = W_B x_q is summed into LDS by every wave; zero it first
         if constexpr (kSetup == kCodes) {
-            for (int e = threadIdx.x; e < 16 * kRank; e += W * kWave) (&tsum[0][0])[e] = 0;
+            for (int e = tid; e < 16 * kRank; e += W * kWave) (&tsum[0][0])[e] = 0;
             lds_barrier();
         }
         // token scales and the LoRA down-projection: loaded now, stored to LDS after the
@@ -402,7 +396,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         float tv[U], sbv[U];
 #pragma unroll
         for (int q = 0; q < U; ++q) {
-            const int e = threadIdx.x + q * W * kWave;
+            const int e = tid + q * W * kWave;
             const int tok = e / kRank, r = e % kRank;
             const bool live = e < 16 * kRank;  // tokens past M fall past t's range
             tv[q] = kSetup == kGivenT ? (float)(int32_t)__builtin_amdgcn_raw_buffer_load_b32(
@@ -412,7 +406,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         }
         // token scales past M read zero (buffer range of M floats)
         const float sxv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            make_rsrc(s_x, (uint32_t)(M * 4)), 4 * (threadIdx.x < 16 ? (int)threadIdx.x : 16), 0, 0));
+            make_rsrc(s_x, (uint32_t)(M * 4)), 4 * (tid < 16 ? tid : 16), 0, 0));
 
         // Activations of token i in bit-plane order, for this lane's chunks.  With one
         // chunk per lane its loads go out ahead of the first row's epilogue operands and
@@ -428,7 +422,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         const int xoff = kFast ? i * (int)K : 0;
         // kCodes: W_B row i (rank i) over the same k as token i's codes, the A operand of
         // the t MFMAs (B = the codes in natural order): D[4g + v][i] = t[token i][rank 4g + v]
-        const int8_t* wb_p = kSetup == kCodes ? fio.w_b + (int64_t)blockIdx.y * kRank * K : x_q;
+        const int8_t* wb_p = kSetup == kCodes ? fio.w_b + prob * kRank * K : x_q;
         const __amdgpu_buffer_rsrc_t wb_rsrc =
             make_rsrc(wb_p, (kSetup == kCodes && kFast) ? (uint32_t)(kRank * K) : 0u);
         const uint8_t* wbrow = reinterpret_cast<const uint8_t*>(wb_p) + (int64_t)i * K;
@@ -450,7 +444,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
             }
         }
         if constexpr (C > 1) {
-            load_first_row();
+            issue_rows();
             prefetch_first_stages();
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -484,7 +478,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
             }
             if constexpr (C == 1) {
                 __builtin_amdgcn_sched_barrier(0);  // the activation loads go out first
-                load_first_row();
+                issue_rows();
                 prefetch_first_stages();
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -521,36 +515,69 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
             // LoRA: u[tok][r] = s_B[r] * t[tok][r] (fp32), shared by every output row.
 #pragma unroll
             for (int q = 0; q < U; ++q) {
-                const int e = threadIdx.x + q * W * kWave;
+                const int e = tid + q * W * kWave;
                 u[e < 16 * kRank ? e : 16 * kRank] = sbv[q] * tv[q];
             }
         }
-        sxs[threadIdx.x < 16 ? threadIdx.x : 16] = sxv;
+        sxs[tid < 16 ? tid : 16] = sxv;
         xs_part[wave][lane] = xpart;
-        for (int e = threadIdx.x; e < 2 * T * 16 * 20; e += W * kWave) (&red[0][0][0])[e] = 0;
+        for (int e = tid; e < 2 * T * 16 * 20; e += W * kWave) (&red[0][0][0])[e] = 0;
         lds_barrier();
         if constexpr (kSetup == kCodes) {
             // u from the summed t; the problem's first group also writes t when asked to
             const bool writer = blockIdx.x == 0 && fio.t != nullptr && rank != 0;
 #pragma unroll
             for (int q = 0; q < U; ++q) {
-                const int e = threadIdx.x + q * W * kWave;
+                const int e = tid + q * W * kWave;
                 if (e < 16 * kRank) {
                     const int tok = e / kRank, r = e % kRank;
                     const int32_t tt = tsum[tok][r];
                     u[e] = tok < M ? sbv[q] * (float)tt : 0.0f;
-                    if (writer && tok < M) fio.t[((int64_t)blockIdx.y * M + tok) * kRank + r] = tt;
+                    if (writer && tok < M) fio.t[(prob * M + tok) * kRank + r] = tt;
                 }
             }
         }
-        if (threadIdx.x < 16) {
+        if (tid < 16) {
             int32_t s = 0;
             for (int w = 0; w < W; ++w)
-                for (int gg = 0; gg < 4; ++gg) s += xs_part[w][16 * gg + threadIdx.x];
-            xsum[threadIdx.x] = s;
+                for (int gg = 0; gg < 4; ++gg) s += xs_part[w][16 * gg + tid];
+            xsum[tid] = s;
         }
-        store_rows();
-        // (xsum and the row operands are read after the first stage's barrier below)
+        // (xsum is read after the first stage's barrier below)
+    }
+
+    // The LoRA up-projection of every row the group owns, once, for up to 4 tokens:
+    // lora[n][tok] = sum_r W_A[n][r] u[tok][r] -- the fmaf chain the per-element form
+    // runs, in the same order -- written over the row's W_A in LDS (16 bytes either
+    // way), so that each stage's epilogue reads one value instead of running the
+    // 16-term chain (with more tokens the epilogue still runs it).  The barrier makes u
+    // and every wave's row operands (their LDS loads waited for by its fence) visible.
+    const bool lora_pre = M <= 4;
+    if (lora_pre) {
+        lds_barrier();
+        for (int r = tid; r < nrows; r += kSubThreads) {
+            // (u is re-read per row: hoisted out of the loop, 4 x 16 values would stay
+            // live across it and push the kernel's registers past its budget)
+            asm volatile("" ::: "memory");
+            const uint4 wa = wa_lds[r];
+            const uint32_t words[4] = {wa.x, wa.y, wa.z, wa.w};
+            float l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int tok = 0; tok < 4; ++tok) {
+                if (tok < M) {  // uniform
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < kRank; ++q) {
+                        const float a = (float)(int8_t)(words[q >> 2] >> (8 * (q & 3)));
+                        acc = fmaf(a, u[tok * kRank + q], acc);
+                    }
+                    l[tok] = acc;
+                }
+            }
+            wa_lds[r] = make_uint4(__float_as_uint(l[0]), __float_as_uint(l[1]), __float_as_uint(l[2]),
+                                   __float_as_uint(l[3]));
+        }
+        // (read by the epilogues after the first stage's barrier)
     }
 
     // Outputs through buffer resources: dead elements store to an out-of-range offset.
@@ -604,7 +631,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         // Epilogue element (row erow of the stage, tokens etok0 + q kTokStride): the
         // thread-to-element map rotates by one wave per stage, so with few tokens the
         // waves (and SIMDs) that carry the epilogue change from stage to stage.
-        const int rtid = (int)((threadIdx.x + (st % W) * kWave) % (W * kWave));
+        const int rtid = (int)((tid + (st % W) * kWave) % (W * kWave));
         const int erow = rtid % (T * 16), etok0 = rtid / (T * 16);
         const int64_t n = st * T * 16 + erow;
         const int lrow = (int)(n - row0);
@@ -618,17 +645,28 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
                 const int32_t s1 = red[rb][erow][tok];
                 red[rb][erow][tok] = 0;  // ready for the stage after next
                 const int32_t acc_pm = 2 * s1 - xsum[tok];
-                // LoRA up (u and W_A are zero at rank 0, leaving the scaffold term exact)
+                // LoRA up (u and W_A are zero at rank 0, leaving the scaffold term exact):
+                // precomputed per row for up to 4 tokens, else the chain here
                 float lora = 0.0f;
+                if (lora_pre) {
+                    lora = __uint_as_float(words[tok & 3]);
+                } else {
 #pragma unroll
-                for (int r = 0; r < kRank; ++r) {
-                    const float a = (float)(int8_t)(words[r >> 2] >> (8 * (r & 3)));
-                    lora = fmaf(a, u[tok * kRank + r], lora);
+                    for (int r = 0; r < kRank; ++r) {
+                        const float a = (float)(int8_t)(words[r >> 2] >> (8 * (r & 3)));
+                        lora = fmaf(a, u[tok * kRank + r], lora);
+                    }
                 }
                 const float inner = fmaf(sa, lora, sw * (float)acc_pm);
                 const int off = n < N ? (int)(((int64_t)tok * N + n) * 4) : kOffDead;
                 store_i32(acc_pm, acc_rsrc, off);
-                store_f32(sxs[tok] * inner, y_rsrc, off);
+                if (lora_pre) {
+                    // y waits in the row's slot, in place of the LoRA value just read
+                    // (each slot word is one element's), until the group's last stage
+                    reinterpret_cast<float*>(&wa_lds[lrow])[tok & 3] = sxs[tok] * inner;
+                } else {
+                    store_f32(sxs[tok] * inner, y_rsrc, off);
+                }
             }
         }
         // No second barrier: the next stage adds into the other buffer, and this one is
@@ -642,6 +680,19 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         run_stage(st, s0, s2, rb);
         run_stage(st + 1, s1, s0, rb ^ 1);
         run_stage(st + 2, s2, s1, rb);
+    }
+    // y of the group's rows, held in LDS by the epilogues, leaves in one pass:
+    // interleaved with the packed-sign stream, the small scattered stores cost the
+    // stream far more than their bytes (the HBM turns between reads and writes)
+    if (lora_pre) {
+        lds_barrier();
+        for (int tok = 0; tok < M; ++tok) {  // uniform
+            for (int r = tid; r < nrows; r += kSubThreads) {
+                const int64_t n = row0 + r;
+                store_f32(reinterpret_cast<const float*>(&wa_lds[r])[tok], y_rsrc,
+                          n < N ? (int)(((int64_t)tok * N + n) * 4) : kOffDead);
+            }
+        }
     }
 }
 
