@@ -58,8 +58,10 @@ struct FusedIO {
 
 // Rows one workgroup owns at most (their epilogue operands live in LDS): 2048 for the
 // 8-wave, 4-tile-stage shape that large batches run (one group per 2048-row problem),
-// 1024 otherwise, which keeps more of the smaller groups resident per CU.
-constexpr int gemv_rows_cap(int W, int T) { return (W >= 8 && T >= 4) ? 2048 : 1024; }
+// 1088 (17 stages of 64 rows) otherwise, which keeps four 4-wave groups resident per CU
+// and splits a 8512-row problem into 8 groups (two resident rounds over 256 problems).
+// A multiple of 64: the row loads fill whole 64-row slots.
+constexpr int gemv_rows_cap(int W, int T) { return (W >= 8 && T >= 4) ? 2048 : 1088; }
 
 // One lane group = 16 lanes; one chunk = 16 packed bytes = 128 k of one row.
 // W waves split K; C chunks per lane; T row tiles (16 rows each) per stage.
@@ -75,7 +77,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
     const uint8_t* __restrict__ w_bits, const float* __restrict__ s_w,
     const int8_t* __restrict__ w_a, const float* __restrict__ s_a, const float* __restrict__ s_b,
     const int32_t* __restrict__ t, int rank, float* __restrict__ y, int32_t* __restrict__ acc_dbg,
-    int64_t num_tiles, int stages_per_wg, FusedIO fio) {
+    int64_t num_tiles, FusedIO fio) {
     constexpr bool kFused = kSetup == kQuantize;
     static_assert(!kFused || (kFast && C == 1), "the fused setup needs whole 128-k chunks, one per lane");
     constexpr int kSubThreads = W * kWave;
@@ -132,8 +134,10 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
     const int g = lane >> 4;
     const int64_t RB = K / 8;
     const int64_t num_stages = (num_tiles + T - 1) / T;
-    const int64_t st_begin = (int64_t)blockIdx.x * stages_per_wg;
-    const int64_t st_end = st_begin + stages_per_wg < num_stages ? st_begin + stages_per_wg : num_stages;
+    // the problem's stages split evenly over its gridDim.x groups (counts differ by one at
+    // most; the host keeps every group within its rows cap and at least one stage)
+    const int64_t st_begin = (int64_t)blockIdx.x * num_stages / gridDim.x;
+    const int64_t st_end = (int64_t)(blockIdx.x + 1) * num_stages / gridDim.x;
 
     // packed-sign loads of one stage: T tiles x C chunks, 16 bytes per lane.  The fast
     // path loads through a buffer resource over this problem's signs: offsets advance
@@ -739,19 +743,28 @@ static hipError_t launch_gemv_wct(bool fast, int setup, const int8_t* x_q, const
         resident_wgs = fast ? gemv_resident<W, C, T, true, kGivenT>() : gemv_resident<W, C, T, false, kGivenT>();
     }
     const bool throughput = batch * num_stages >= 4 * resident_wgs;
-    const int64_t target_wgs = throughput ? resident_wgs : (setup != kGivenT ? 256 : 2048);
-    const int64_t per_problem = (target_wgs + batch - 1) / batch;
-    int stages_per_wg = (int)((num_stages + per_problem - 1) / per_problem);
     constexpr int kRowsCap = gemv_rows_cap(W, T);
-    if (stages_per_wg * T * 16 > kRowsCap) stages_per_wg = kRowsCap / (T * 16);
-    const dim3 grid((unsigned)((num_stages + stages_per_wg - 1) / stages_per_wg), (unsigned)batch);
+    constexpr int64_t kMaxStages = kRowsCap / (T * 16);
+    int64_t per_problem;
+    if (throughput) {
+        // whole resident rounds: as few as the rows cap allows, their groups spread
+        // evenly over the problems (and a problem's stages evenly over its groups)
+        const int64_t rounds = (batch * num_stages + resident_wgs * kMaxStages - 1) / (resident_wgs * kMaxStages);
+        per_problem = (rounds * resident_wgs + batch - 1) / batch;
+    } else {
+        const int64_t target_wgs = setup != kGivenT ? 256 : 2048;
+        per_problem = (target_wgs + batch - 1) / batch;
+    }
+    const int64_t min_groups = (num_stages + kMaxStages - 1) / kMaxStages;  // the rows cap
+    if (per_problem < min_groups) per_problem = min_groups;
+    if (per_problem > num_stages) per_problem = num_stages;
+    const dim3 grid((unsigned)per_problem, (unsigned)batch);
     // In the throughput regime the one-call form pays off only with one group per
     // problem: every further group would quantize the tokens and read W_B again.
     if (setup == kQuantize && throughput && grid.x > 1) return hipErrorNotSupported;
 #define DFSSM_GEMV_LAUNCH(FAST, SETUP)                                                                        \
     gemv_kernel<W, C, T, FAST, SETUP><<<grid, W * kWave, 0, stream>>>(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, \
-                                                                      s_b, t, rank, y, acc_dbg, num_tiles,      \
-                                                                      stages_per_wg, fio)
+                                                                      s_b, t, rank, y, acc_dbg, num_tiles, fio)
     if (setup == kQuantize) {
         if constexpr (C == 1) DFSSM_GEMV_LAUNCH(true, kQuantize);
     } else if (setup == kCodes) {
