@@ -37,6 +37,18 @@
 
 namespace dfssm {
 
+// A workgroup barrier for the setup's LDS exchanges only: this wave's LDS operations
+// complete (lgkmcnt), then the barrier, with the compiler kept from moving memory
+// operations across it.  Unlike lds_barrier's release fence it does not wait for the
+// rows' LDS-destination loads still in flight (they are waited for by the lds_barrier
+// ahead of their first use), so the setup's steps overlap their arrival.
+__device__ __forceinline__ void setup_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left alone
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Where a group's setup takes the tokens' codes and the LoRA down-projection from:
 //  kGivenT   x_q and t = W_B x_q are inputs (t from a LoRA-down call);
 //  kQuantize x is the input: the setup quantizes the tokens and computes t itself (the
@@ -243,11 +255,16 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         const bool chunk_live = 128 * qch < K;   // K % 128 == 0: whole chunks only
         const __amdgpu_buffer_rsrc_t wb_rsrc =
             make_rsrc(rank != 0 ? fio.w_b + p * kRank * K : fio.w_b, rank != 0 ? (uint32_t)(kRank * K) : 0u);
+        // W_B for t: the contraction's k order is free (the codes are read from LDS in
+        // the same order), so piece e of lane group g is bytes 512 wave + 64 e + 16 g of
+        // row i -- each instruction reads 64 contiguous bytes of every row, not sixteen
+        // scattered pieces per 128-byte line; pieces past K read zero
+        auto t_k = [&](int e) __attribute__((always_inline)) { return 512 * wave + 64 * e + 16 * g; };
         v4i wbv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             wbv[e] = __builtin_amdgcn_raw_buffer_load_b128(
-                wb_rsrc, chunk_live ? (int)(i * K + 128 * qch + 16 * e) : kOffDead - 64, 0, 0);
+                wb_rsrc, t_k(e) < K ? (int)(i * K + t_k(e)) : kOffDead - 64, 0, 0);
         const __amdgpu_buffer_rsrc_t sb_rsrc = make_rsrc(s_b, rank != 0 ? (uint32_t)(kRank * 4) : 0u);
         float sbv[U];
 #pragma unroll
@@ -284,7 +301,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
                 if (lane == 0) amax_part[wave][mm] = w;
             }
         }
-        lds_barrier();
+        setup_barrier();
         float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, inv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, amx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         bool fast[4] = {false, false, false, false};
 #pragma unroll
@@ -326,14 +343,21 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
             sxs[tid] = s;
             if (writer && tid < M) fio.s_x[p * M + tid] = s;
         }
-        lds_barrier();
+        setup_barrier();
 
-        // this lane's chunk of token i's codes, two 16-byte pieces at a time: the t
-        // MFMAs take them in natural order, the scaffold operand in bit-plane order
+        // token i's codes: t's pieces (in W_B's order above), and this lane's chunk two
+        // 16-byte pieces at a time for the scaffold operand (bit-plane order)
         const uint8_t* crow = reinterpret_cast<const uint8_t*>(codes_lds) + (i < M ? i * K : 0);
         const bool xlive = i < M && chunk_live;
         int32_t xpart = 0;
         v4i acc_t = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint4 v = (i < M && t_k(e) < K) ? *reinterpret_cast<const uint4*>(crow + t_k(e))
+                                                  : make_uint4(0u, 0u, 0u, 0u);
+            const v4i bv = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+            acc_t = __builtin_amdgcn_mfma_i32_16x16x64_i8(wbv[e], bv, acc_t, 0, 0, 0);
+        }
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
             uint32_t nat[8];
@@ -346,8 +370,6 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
                 nat[4 * h + 1] = v.y;
                 nat[4 * h + 2] = v.z;
                 nat[4 * h + 3] = v.w;
-                const v4i bv = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-                acc_t = __builtin_amdgcn_mfma_i32_16x16x64_i8(wbv[e], bv, acc_t, 0, 0, 0);
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) xpart = byte_sum(nat[e], xpart);
@@ -367,7 +389,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
             for (int v = 0; v < 4; ++v) atomicAdd(&tsum[i][4 * g + v], acc_t[v]);
         }
         xs_part[wave][lane] = xpart;
-        lds_barrier();
+        setup_barrier();
 #pragma unroll
         for (int q = 0; q < U; ++q) {
             const int e = tid + q * NT;
@@ -389,7 +411,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         // kCodes: t = W_B x_q is summed into LDS by every wave; zero it first
         if constexpr (kSetup == kCodes) {
             for (int e = tid; e < 16 * kRank; e += W * kWave) (&tsum[0][0])[e] = 0;
-            lds_barrier();
+            setup_barrier();
         }
         // token scales and the LoRA down-projection: loaded now, stored to LDS after the
         // activation loads below have been issued too
@@ -526,7 +548,7 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         sxs[tid < 16 ? tid : 16] = sxv;
         xs_part[wave][lane] = xpart;
         for (int e = tid; e < 2 * T * 16 * 20; e += W * kWave) (&red[0][0][0])[e] = 0;
-        lds_barrier();
+        setup_barrier();
         if constexpr (kSetup == kCodes) {
             // u from the summed t; the problem's first group also writes t when asked to
             const bool writer = blockIdx.x == 0 && fio.t != nullptr && rank != 0;
