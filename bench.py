@@ -220,6 +220,76 @@ def profiled_launch():
     return {k: rec[k] for k in ("avg_us", "median_us", "launches", "command") if k in rec}
 
 
+UTIL_FILE = os.path.join(ROOT, "profiles", "counters_utilization_bench.md")
+UTIL_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
+                 "SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+UTIL_CMD = ("rocprofv3 --pmc " + " ".join(UTIL_COUNTERS) + " -d gpurun_out/pmc_util -o run --output-format csv -- "
+            "python -u bench.py --steps 5 --warmup 2 --settle-seconds 0 --prefill-iters 3 --no-cpu-baseline "
+            "--no-sweeps")
+
+
+def util_from(counter_csv):
+    """Per-kernel MFMA / VALU / LDS utilization from one counter pass (UTIL_CMD), as the
+    summary table under profiles/."""
+    disp = {}
+    with open(counter_csv) as fh:
+        for r in csv.DictReader(fh):
+            d = disp.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"], "grid": r["Grid_Size"],
+                                                   "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    def strip_args(name):
+        # drop the trailing parameter list (the parenthesized group that ends the name)
+        name = name.strip()
+        if name.endswith(")"):
+            depth = 0
+            for k in range(len(name) - 1, -1, -1):
+                depth += {")": 1, "(": -1}.get(name[k], 0)
+                if depth == 0:
+                    name = name[:k]
+                    break
+        return name.replace("void ", "")
+
+    groups = {}
+    for d in disp.values():
+        groups.setdefault((strip_args(d["name"]), d["grid"]), []).append(d)
+    rows = []
+    for (name, grid), ds in groups.items():
+        def tot(c):
+            return sum(x.get(c, 0.0) for x in ds)
+        cycles = tot("GRBM_GUI_ACTIVE") / 8          # summed over the 8 XCDs
+        us = sum(x["us"] for x in ds)
+        if cycles <= 0 or us <= 0:
+            continue
+        rows.append((len(ds), name, grid, us / len(ds),
+                     100 * tot("SQ_VALU_MFMA_BUSY_CYCLES") / (cycles * 1024),
+                     100 * tot("SQ_ACTIVE_INST_VALU") / (cycles * 256),
+                     100 * tot("SQ_LDS_IDX_ACTIVE") / (cycles * 256),
+                     100 * tot("SQ_LDS_BANK_CONFLICT") / (cycles * 256),
+                     512 * tot("SQ_INSTS_VALU_MFMA_MOPS_I8") / (us * 1e-6) / 1e12))
+    rows.sort(key=lambda r: -r[0] * r[3])
+    lines = [
+        "# Hardware counters: MFMA, VALU and LDS utilization per kernel (bench.py, short run)", "",
+        "Command (repository root, one MI355X):", "", "```", UTIL_CMD, "```", "",
+        "Per dispatch, the counters come summed over the GPU's 8 XCDs (GRBM_GUI_ACTIVE too: divided by 8 it "
+        "gives the dispatch's cycles). MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs); VALU "
+        "busy % = SQ_ACTIVE_INST_VALU / (cycles x 256 CUs); LDS active % = SQ_LDS_IDX_ACTIVE / (cycles x 256); "
+        "int8 MFMA TOPS = 512 x SQ_INSTS_VALU_MFMA_MOPS_I8 / duration (one MOPS unit is 512 int8 ops). "
+        "Durations are under counter collection (every dispatch serialized), so they run longer than in "
+        "the bench. `--no-sweeps` leaves out the launch-heavy legs (per-call graphs, 48-layer sweep, chained "
+        "and one-launch decode).", "",
+        "| kernel | grid | dispatches | mean us | MFMA busy % | VALU busy % | LDS active % | "
+        "LDS bank conflict % | int8 MFMA TOPS |",
+        "|---|---|---|---|---|---|---|---|---|",
+    ]
+    for n, name, grid, us, mf, va, lds, bc, tops in rows:
+        short = name if len(name) <= 130 else name[:130]
+        lines.append(f"| `{short}` | {grid} | {n} | {us:.2f} | {mf:.1f} | {va:.1f} | {lds:.1f} | {bc:.2f} | "
+                     f"{tops:.0f} |")
+    with open(UTIL_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"{len(rows)} kernels -> {UTIL_FILE}")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +308,8 @@ def parse():
     ap.add_argument("--prefill-iters", type=int, default=10)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMV traffic record from two rocprofv3 counter_collection.csv files")
+    ap.add_argument("--util-from", metavar="COUNTER_CSV",
+                    help="write the utilization summary from the counter pass of UTIL_CMD")
     ap.add_argument("--profile-from", metavar="KERNEL_TRACE_CSV",
                     help="write the headline kernel's profile record and the kernel summary from the "
                          "rocprofv3 kernel trace of the default bench")
@@ -670,6 +742,9 @@ def main():
         return
     if args.profile_from:
         profile_from(args.profile_from, args.steps)
+        return
+    if args.util_from:
+        util_from(args.util_from)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the projection is not sharded "
