@@ -7,29 +7,33 @@
 // stateful convolution and SSM recurrence -> out_proj.  Here the launches go away
 // altogether: one persistent grid (one 512-thread group per CU, co-resident by a
 // cooperative launch) walks all layers, and the dependencies between the three steps
-// of a layer become device-wide counters:
+// of a layer become tagged exchanges (below):
 //
 //   phase A (in_proj, K 2048 -> N 8512): every group quantizes the layer's input x
 //     (absmax / 127, ties to even), computes t = W_B x_q for itself, and produces its
-//     33 or 34 rows of zxbcdt; then it counts itself in A[l].
-//   phase B (Mamba-2 step): group g owns 16 channels of head g / 4; once A[l] reaches
-//     the group count it reads its z, x, dt and the shared B, C, runs the convolution,
-//     the state update and the gate, g = y silu(z), for its channels; counts in B[l].
-//   phase C (gated RMS norm + out_proj, K 4096 -> N 2048): once B[l] is full, every
-//     group reads all of g, forms the norm (the mean square in one fixed order, so all
-//     groups get the same bits), quantizes the result, computes t, and produces its 8
-//     rows of the next layer's input; counts in C[l], which phase A of layer l + 1
-//     waits for.
+//     33 or 34 rows of zxbcdt.
+//   phase B (Mamba-2 step): group g owns 16 channels of head g / 4; it reads its z, x,
+//     dt and the shared B, C, runs the convolution, the state update and the gate,
+//     g = y silu(z), for its channels.
+//   phase C (gated RMS norm + out_proj, K 4096 -> N 2048): every group reads all of g,
+//     forms the norm (the mean square in one fixed order, so all groups get the same
+//     bits), quantizes the result, computes t, and produces its 8 rows of the next
+//     layer's input.
+//
+// Exchanges: each produced value travels with a tag in one 8-byte device-scope store
+// (write-through, coherent across the XCDs' L2s without cache-maintenance fences; an
+// aligned 8-byte store is one access, so a reader that sees the tag sees the value
+// stored with it).  The tag names the call, the layer and the phase; readers poll the
+// pairs they need until the tags are current -- no counters, no waiting for store
+// completions.  The slots are double-buffered by layer parity: a slot is written again
+// two layers later, which the data dependencies order after every read of it.  Every
+// wait is bounded: past the poll limit, or once any group has reported a failure, it
+// gives up and ORs a bit into the caller's status word; the kernel always runs to the
+// end.  The last group to finish advances the call counter that the tags carry.
 //
 // Weights do not depend on activations, so each group issues the loads of its next
 // phase's packed signs, W_B slice, epilogue operands and state slice before it waits:
-// the HBM stream overlaps the wait.  Exchanged activations are written with
-// device-scope (write-through) stores and read with device-scope loads, so they are
-// coherent across the XCDs' L2s without cache-maintenance fences; a group counts
-// itself only after its stores have completed.  Every wait is bounded: past the
-// poll limit, or once any group has reported a failure, it gives up and ORs a bit
-// into the caller's status word; the kernel always runs to the end.  The last group
-// to finish resets the counters, so the workspace is ready for the next call.
+// the HBM stream overlaps the wait.
 //
 // At M = 1 the products are latency-bound, so they run on the vector ALUs: the packed
 // signs are expanded by bit plane (w & (0x01010101 << j) holds four weights of plane
@@ -48,16 +52,19 @@ constexpr int kDModel = 2048, kDInner = 4096, kDState = 128, kNHeads = 64, kHead
 constexpr int kConvDim = kDInner + 2 * kDState;            // 4352
 constexpr int kNIn = kDInner + kConvDim + kNHeads;          // 8512
 constexpr int kGroups = 256, kThreads = 512, kWaves = kThreads / kWave;
-constexpr int kCtrStride = 16;                               // words between counters (64 B)
+constexpr int kCtrStride = 16;                               // words per counter slot (64 B)
 constexpr int kMaxLayers = 64;
 constexpr int kStatusTimeout = 1, kStatusGaveUp = 2;
 
-// workspace layout (4-byte words)
-constexpr int kWsCounters = 0;                               // (3 kMaxLayers + 1) counters
-constexpr int kWsX = (3 * kMaxLayers + 1) * kCtrStride;      // x [2][2048]
-constexpr int kWsZx = kWsX + 2 * kDModel;                    // zxbcdt [2][8512]
-constexpr int kWsG = kWsZx + 2 * kNIn;                       // g [2][4096]
-constexpr int kWsWords = kWsG + 2 * kDInner;
+// workspace layout (4-byte words): the count of groups done (the last one resets it),
+// the call counter (it tags every exchanged value), then the exchange slots as
+// (value, tag) pairs, double-buffered by layer parity
+constexpr int kWsDone = 0;
+constexpr int kWsGen = kCtrStride;
+constexpr int kWsX = 2 * kCtrStride;                         // x      [2][2048] pairs
+constexpr int kWsZx = kWsX + 2 * 2 * kDModel;                // zxbcdt [2][8512] pairs
+constexpr int kWsG = kWsZx + 2 * 2 * kNIn;                   // g      [2][4096] pairs
+constexpr int kWsWords = kWsG + 2 * 2 * kDInner;
 
 // trace layout per layer (4-byte words)
 constexpr int kTrZx = 0, kTrOut = kTrZx + kNIn, kTrXn = kTrOut + kDInner, kTrAccIn = kTrXn + kDModel,
@@ -69,60 +76,79 @@ constexpr int kTrZx = 0, kTrOut = kTrZx + kNIn, kTrXn = kTrOut + kDInner, kTrAcc
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 __device__ __forceinline__ float softplus(float v) { return v > 20.0f ? v : log1pf(expf(v)); }
 
-// device-scope (coherent across XCDs) exchange loads and stores
-__device__ __forceinline__ float4 ld4_dev(const float* base, uint32_t bytes, int byte_off) {
-    const v4f v = __builtin_bit_cast(
-        v4f, __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(base, bytes), byte_off, 0, kAuxDeviceScope));
-    return make_float4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ float ld_dev(const float* base, uint32_t bytes, int byte_off) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(base, bytes), byte_off, 0, kAuxDeviceScope));
+// ---- tagged exchanges (device scope: coherent across the XCDs' L2s)
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+
+// The tag of the values phase `phase` of layer l writes in call `gen` (never 0, so a
+// zeroed slot never passes; L <= 64 keeps the layers of one call apart).
+__device__ __forceinline__ uint32_t xtag(uint32_t gen, int l, int phase) {
+    return ((gen + 1u) << 8) + 4u * (uint32_t)l + (uint32_t)phase;
 }
 
-// Every store of this thread has completed (stores count in vmcnt on gfx9-family parts;
-// device-scope stores complete once written through).
-__device__ __forceinline__ void wait_stores() {
-    __builtin_amdgcn_s_waitcnt(0);
-    asm volatile("" ::: "memory");
+// One value and its tag, in one 8-byte store.
+__device__ __forceinline__ void store_pair(float v, uint32_t tag, __amdgpu_buffer_rsrc_t r, int byte_off) {
+    const v2i_t q = {(int)__float_as_uint(v), (int)tag};
+    __builtin_amdgcn_raw_buffer_store_b64(q, r, byte_off, 0, kAuxDeviceScope);
 }
 
-// Bounded wait of the whole group until *ctr >= target (thread 0 polls).  Returns false
-// once the group has failed (then it no longer waits).
-__device__ bool group_wait(const Args& a, uint32_t* ctr, uint32_t target, bool ok, int* sflag) {
-    if (threadIdx.x == 0) {
-        int fail = ok ? 0 : 1;
-        if (ok) {
-            const uint32_t want = target + a.target_bias;
-            for (int64_t n = 0;; ++n) {
-                const uint32_t v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (v >= want) break;
-                if (n >= a.spin_limit) {
-                    __hip_atomic_fetch_or(a.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    fail = 1;
-                    break;
-                }
-                if ((n & 15) == 15 &&
-                    __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-                    __hip_atomic_fetch_or(a.status, kStatusGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    fail = 1;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
-        *sflag = fail;
+// One round of a bounded wait: counts it, gives up past the poll limit or once the
+// status word shows a failure elsewhere (checked every 16 rounds; either way this
+// thread ORs its reason into the status word), else sleeps briefly.  False: give up.
+__device__ __forceinline__ bool poll_round(const Args& a, int64_t& n) {
+    ++n;
+    if (n >= a.spin_limit) {
+        __hip_atomic_fetch_or(a.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
     }
-    lds_barrier();
-    const bool r = *sflag == 0;
-    lds_barrier();  // the flag slot is reused by the next wait
-    return r;
+    if ((n & 15) == 15 && __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+        __hip_atomic_fetch_or(a.status, kStatusGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    return true;
 }
 
-// Count the group in *ctr once every thread's stores have completed.
-__device__ __forceinline__ void group_signal(uint32_t* ctr) {
-    wait_stores();
-    lds_barrier();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// P consecutive 16-byte pieces (two pairs each) from byte offset `off`, all written by
+// one producer at one moment: the first piece is polled until both its tags equal
+// `want`, then the rest are read together (and any still stale is polled alone).
+// Returns false once this thread has given up (its later waits then only read).
+template <int P>
+__device__ bool read_pieces(const Args& a, __amdgpu_buffer_rsrc_t r, int off, uint32_t want, float (&v)[2 * P],
+                            bool ok) {
+    int64_t n = 0;
+    for (;;) {
+        const v4i q = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxDeviceScope);
+        v[0] = __int_as_float(q[0]);
+        v[1] = __int_as_float(q[2]);
+        if (((uint32_t)q[1] == want && (uint32_t)q[3] == want) || !ok) break;
+        ok = poll_round(a, n);
+    }
+    v4i q[P > 1 ? P - 1 : 1];
+#pragma unroll
+    for (int p = 1; p < P; ++p) q[p - 1] = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * p, 0, kAuxDeviceScope);
+#pragma unroll
+    for (int p = 1; p < P; ++p) {
+        for (;;) {
+            v[2 * p] = __int_as_float(q[p - 1][0]);
+            v[2 * p + 1] = __int_as_float(q[p - 1][2]);
+            if (((uint32_t)q[p - 1][1] == want && (uint32_t)q[p - 1][3] == want) || !ok) break;
+            ok = poll_round(a, n);
+            q[p - 1] = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * p, 0, kAuxDeviceScope);
+        }
+    }
+    return ok;
+}
+
+// One pair, polled until its tag equals `want`.
+__device__ bool read_pair(const Args& a, __amdgpu_buffer_rsrc_t r, int off, uint32_t want, float& v, bool ok) {
+    int64_t n = 0;
+    for (;;) {
+        const v2i_t q = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kAuxDeviceScope);
+        v = __int_as_float(q[0]);
+        if ((uint32_t)q[1] == want || !ok) break;
+        ok = poll_round(a, n);
+    }
+    return ok;
 }
 
 // Maximum over the group (every thread gets it): one barrier; `red` is not reused
@@ -197,7 +223,6 @@ struct Lds {
     int32_t tsl[kRank];             // t
     float xs[16], ys[16], Bs[kDState], Cs[kDState];
     float dt_h;
-    int flag;
 };
 
 // The codes of V float4 pieces per thread (absmax / 127, ties to even), with the
@@ -249,10 +274,12 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
     const int g = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
-    uint32_t* const ctr = a.ws + kWsCounters;
-    float* const xbuf = reinterpret_cast<float*>(a.ws + kWsX);
-    float* const zxbuf = reinterpret_cast<float*>(a.ws + kWsZx);
-    float* const gbuf = reinterpret_cast<float*>(a.ws + kWsG);
+    // the exchange slots, (value, tag) pairs; slot parity p of each at p * (its pairs)
+    const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(a.ws + kWsX, 2 * 2 * kDModel * 4);
+    const __amdgpu_buffer_rsrc_t zx_rsrc = make_rsrc(a.ws + kWsZx, 2 * 2 * kNIn * 4);
+    const __amdgpu_buffer_rsrc_t g_rsrc = make_rsrc(a.ws + kWsG, 2 * 2 * kDInner * 4);
+    // this call's number (every group reads it before any group can advance it)
+    const uint32_t gen = __hip_atomic_load(a.ws + kWsGen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     bool ok = true;
 
     // ---- this group's fixed roles
@@ -303,8 +330,11 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
         if (l == 0) {
             xv[0] = reinterpret_cast<const float4*>(a.x_in)[tid];
         } else {
-            ok = group_wait(a, ctr + (3 * (l - 1) + 2) * kCtrStride, kGroups, ok, &s.flag);
-            xv[0] = ld4_dev(xbuf + (l & 1) * kDModel, kDModel * 4, 16 * tid);
+            // x[4 tid .. 4 tid + 3], from the group that wrote rows 8 (tid / 2) ..
+            float v[4];
+            ok = read_pieces<2>(a, x_rsrc, 8 * ((l & 1) * kDModel + 4 * tid), xtag(gen, l - 1, 2) + a.target_bias,
+                                v, ok);
+            xv[0] = make_float4(v[0], v[1], v[2], v[3]);
         }
         // quantize: the absmax, then the codes in natural order
         const float amaxA = group_max(absmax4(xv[0]), s.red_max);
@@ -358,14 +388,14 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
                 for (int r = 0; r < kRank; ++r)
                     lora = fmaf((float)(int8_t)(words[r >> 2] >> (8 * (r & 3))), sbA[r] * (float)s.tsl[r], lora);
                 const float y = sxA * fmaf(saA, lora, swA * (float)acc);
-                store_f32_dev(y, make_rsrc(zxbuf + (l & 1) * kNIn, kNIn * 4), 4 * na);
+                store_pair(y, xtag(gen, l, 0), zx_rsrc, 8 * ((l & 1) * kNIn + na));
                 if (a.trace) {
                     a.trace[(int64_t)l * kTrWords + kTrZx + na] = __float_as_uint(y);
                     a.trace[(int64_t)l * kTrWords + kTrAccIn + na] = (uint32_t)acc;
                 }
             }
         }
-        group_signal(ctr + (3 * l + 0) * kCtrStride);
+        lds_barrier();  // the phase's LDS is free for the next
 
         // ======================= phase B: Mamba-2 step =======================
         float4* const stp = reinterpret_cast<float4*>(
@@ -381,13 +411,18 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
         }
         const float dtb = a.dt_bias[(int64_t)l * kNHeads + h], alog = a.A_log[(int64_t)l * kNHeads + h];
         const float dph = a.Dp[(int64_t)l * kNHeads + h];
-        ok = group_wait(a, ctr + (3 * l + 0) * kCtrStride, kGroups, ok, &s.flag);
         {
-            const float* zx = zxbuf + (l & 1) * kNIn;
+            // this group's rows of zxbcdt, each polled until phase A of this layer wrote it
+            const uint32_t want = xtag(gen, l, 0) + a.target_bias;
+            const int zx0 = (l & 1) * kNIn;
             float xn = 0.0f, zv = 0.0f;
-            if (conv_live) xn = ld_dev(zx, kNIn * 4, 4 * (kDInner + conv_c));
-            if (tid < 16) zv = ld_dev(zx, kNIn * 4, 4 * (ch0 + tid));
-            if (tid == 0) s.dt_h = ld_dev(zx, kNIn * 4, 4 * (kDInner + kConvDim + h));
+            if (conv_live) ok = read_pair(a, zx_rsrc, 8 * (zx0 + kDInner + conv_c), want, xn, ok);
+            if (tid < 16) ok = read_pair(a, zx_rsrc, 8 * (zx0 + ch0 + tid), want, zv, ok);
+            if (tid == 0) {
+                float dtv = 0.0f;
+                ok = read_pair(a, zx_rsrc, 8 * (zx0 + kDInner + kConvDim + h), want, dtv, ok);
+                s.dt_h = dtv;
+            }
             if (conv_live) {
                 float acc = cb;
                 acc = fmaf(cw.x, win.y, acc);
@@ -430,10 +465,10 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
             lds_barrier();
             if (tid < 16) {
                 const float gv = s.ys[tid] * silu(zv);
-                store_f32_dev(gv, make_rsrc(gbuf + (l & 1) * kDInner, kDInner * 4), 4 * (ch0 + tid));
+                store_pair(gv, xtag(gen, l, 1), g_rsrc, 8 * ((l & 1) * kDInner + ch0 + tid));
             }
         }
-        group_signal(ctr + (3 * l + 1) * kCtrStride);
+        lds_barrier();  // the phase's LDS is free for the next
 
         // ======================= phase C: norm + out_proj =======================
         const float4* const nw4 = reinterpret_cast<const float4*>(a.norm_w + (int64_t)l * kDInner);
@@ -449,12 +484,14 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
         float sbC[kRank];
 #pragma unroll
         for (int r = 0; r < kRank; ++r) sbC[r] = a.out_sb[(int64_t)l * kRank + r];
-        ok = group_wait(a, ctr + (3 * l + 1) * kCtrStride, kGroups, ok, &s.flag);
         float4 ov[2];
         {
-            const float* gb = gbuf + (l & 1) * kDInner;
-            ov[0] = ld4_dev(gb, kDInner * 4, 32 * tid);
-            ov[1] = ld4_dev(gb, kDInner * 4, 32 * tid + 16);
+            // g[8 tid .. 8 tid + 7], from the group that owns channels 16 (tid / 2) ..
+            float v[8];
+            ok = read_pieces<4>(a, g_rsrc, 8 * ((l & 1) * kDInner + 8 * tid), xtag(gen, l, 1) + a.target_bias, v,
+                                ok);
+            ov[0] = make_float4(v[0], v[1], v[2], v[3]);
+            ov[1] = make_float4(v[4], v[5], v[6], v[7]);
             float ss = 0.0f;
             ss = fmaf(ov[0].x, ov[0].x, ss);
             ss = fmaf(ov[0].y, ov[0].y, ss);
@@ -541,7 +578,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
                 lora = fmaf((float)(int8_t)(words[r >> 2] >> (8 * (r & 3))), sbC[r] * (float)s.tsl[r], lora);
             const float y = sxC * fmaf(saC, lora, swC * (float)acc);
             if (l + 1 < a.L) {
-                store_f32_dev(y, make_rsrc(xbuf + ((l + 1) & 1) * kDModel, kDModel * 4), 4 * nc);
+                store_pair(y, xtag(gen, l, 2), x_rsrc, 8 * (((l + 1) & 1) * kDModel + nc));
             } else {
                 a.x_out[nc] = y;
             }
@@ -550,16 +587,16 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
                 a.trace[(int64_t)l * kTrWords + kTrAccOut + nc] = (uint32_t)acc;
             }
         }
-        group_signal(ctr + (3 * l + 2) * kCtrStride);
+        lds_barrier();  // the phase's LDS is free for the next
     }
 
-    // the last group to finish clears the counters for the next call
+    // the last group to finish advances the call counter (every group has read all it
+    // needs by then) and clears the done count for the next call
     if (tid == 0) {
-        uint32_t* const done = ctr + 3 * kMaxLayers * kCtrStride;
+        uint32_t* const done = a.ws + kWsDone;
         const uint32_t prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (prev == kGroups - 1) {
-            for (int i = 0; i < 3 * a.L; ++i)
-                __hip_atomic_store(ctr + i * kCtrStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.ws + kWsGen, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
@@ -597,8 +634,8 @@ uint32_t* decode_layers_scratch(hipStream_t stream) {
     if (scratch_ptr[dev] == nullptr) {
         void* ptr = nullptr;
         if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
-        // the counters must start at zero (every call leaves them so)
-        zero_words_kernel<<<16, 256, 0, stream>>>(static_cast<uint32_t*>(ptr), decode::kWsX);
+        // the array starts zeroed (the done count, the call counter, no current tags)
+        zero_words_kernel<<<64, 256, 0, stream>>>(static_cast<uint32_t*>(ptr), decode::kWsWords);
         if (hipGetLastError() != hipSuccess) return nullptr;
         scratch_ptr[dev] = static_cast<uint32_t*>(ptr);
     }

@@ -179,8 +179,8 @@ DECODE_HOST_NAMES = {
 class DeviceDecodeStack:
     """A stack of layers on the device for dfssm_decode_layers: the stacked weights, the
     two window buffers (a token reads one and writes the other), the SSM state (updated
-    in place), the counters' workspace (zeroed once here; every call leaves it zeroed)
-    and the status word."""
+    in place), the exchange workspace (zeroed once here, then left to the library: it
+    holds a call counter and the tagged exchange slots) and the status word."""
 
     def __init__(self, stack, device="cuda:0", eps: float = 1e-5):
         def dev(a):

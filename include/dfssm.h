@@ -337,10 +337,13 @@ dfssm_status dfssm_mamba2_decode_step(const float* zxbcdt, int64_t S, int64_t nh
  *     14656, out_proj accumulators int32 [2048] at 23168, x_q of x int8 [2048] at 25216,
  *     x_q of out int8 [4096] at 25728, t of in_proj int32 [16] at 26752, t of out_proj
  *     int32 [16] at 26768, s_x of x and of out fp32 at 26784 and 26785 (verification aid)
- * Synchronization between the layer's three steps is device-wide counters in
- * `workspace` (>= dfssm_decode_layers_workspace_bytes() bytes, 16-byte aligned, zeroed
- * by the caller once before its first use; every call leaves it zeroed again).  Calls
- * that share a workspace must not overlap (the same stream serializes them).
+ * The layer's three steps exchange their outputs through `workspace` (>=
+ * dfssm_decode_layers_workspace_bytes() bytes, 16-byte aligned): each value is stored
+ * with a tag naming the call, the layer and the step, and its readers wait for the tag.
+ * The caller zeroes the workspace once before its first use and then leaves it to the
+ * library between calls (it holds a call counter that the tags carry; re-zeroing it is
+ * allowed only together with all of it).  Calls that share a workspace must not overlap
+ * (the same stream serializes them).
  *   status     int32 in device memory: each wait that gives up ORs a bit in --
  *              DFSSM_DECODE_STATUS_TIMEOUT (its poll limit passed) or
  *              DFSSM_DECODE_STATUS_GAVE_UP (another group had failed); outputs are
@@ -394,9 +397,9 @@ dfssm_status dfssm_decode_layers(const dfssm_decode_layer_weights* w, int64_t n_
  * not call hipMalloc: tight serving loops, harnesses that forbid it).  Same arguments,
  * results and errors, minus the workspace: the library's own array of
  * dfssm_decode_layers_workspace_bytes() bytes per GPU (a file-scope device array, held
- * until the process ends; its counters are cleared on `stream` the first time a device
- * is used, and every call leaves them cleared) serves instead, so nothing is
- * allocated or freed.  The array's size covers the largest stack the call accepts
+ * until the process ends; zeroed on `stream` the first time a device is used) serves
+ * instead, so nothing is allocated or freed.  The array's size covers the largest stack
+ * the call accepts
  * (n_layers <= 64; larger is DFSSM_ERR_INVALID_ARG).  Every call on one GPU shares that
  * GPU's array: calls that overlap on one GPU (other streams, other threads) race, so
  * the caller serializes them (one stream does).  DFSSM_ERR_HIP if the array's device

@@ -25,7 +25,7 @@ from test_gpu_parity import _assert_y, _magnitude, torch_cuda  # noqa: F401  (fi
 pytestmark = pytest.mark.gpu
 
 EPS = 1e-5
-CTR_WORDS = (3 * 64 + 1) * 16   # the workspace's counters (then the exchange buffers)
+DONE_WORD, GEN_WORD = 0, 16     # the workspace's done count and call counter (then the exchange slots)
 TW = dict(zx=(0, 8512), out=(8512, 4096), xn=(12608, 2048), acc_in=(14656, 8512), acc_out=(23168, 2048),
           xq_in=(25216, 512), xq_out=(25728, 1024), t_in=(26752, 16), t_out=(26768, 16), sx=(26784, 2))
 
@@ -93,7 +93,8 @@ def _run(stack, tokens=1, layers=None):
                      range(stack.L) if layers is None else layers)
         conv, ssm = conv_out, ssm_out
         x = x_out.clone()
-    assert not dev.workspace[:CTR_WORDS].any(), "the counters are left zeroed"
+    assert int(dev.workspace[DONE_WORD]) == 0, "the done count is left zeroed"
+    assert int(dev.workspace[GEN_WORD]) == tokens, "the call counter advances once per call"
     return dev
 
 
@@ -143,7 +144,8 @@ def test_decode_layers_bounded_waits_end_the_kernel(torch_cuda):
     torch.cuda.synchronize()
     status = int(dev.status.item())
     assert status & dfssm.DFSSM_DECODE_STATUS_TIMEOUT, status
-    assert not dev.workspace[:CTR_WORDS].any(), "the counters are reset even after a failed call"
+    assert int(dev.workspace[DONE_WORD]) == 0, "the done count is reset even after a failed call"
+    assert int(dev.workspace[GEN_WORD]) == 1, "the failed call still advanced the call counter"
     dev.status.zero_()
     dev.ssm_state.copy_(ssm0)
     tr = dev.new_trace()
