@@ -602,8 +602,8 @@ def decode_persistent_48l(torch, dev, tokens):
             "frac_of_hbm_peak": round(token_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "tokens_timed": tokens, "status": status,
             "note": "dfssm_decode_layers: one cooperative launch of 256 x 512 threads per token; per layer "
-                    "in_proj, Mamba-2 step, gated norm + out_proj, separated by device-wide counters; weights "
-                    "and state prefetched while waiting"}
+                    "in_proj, Mamba-2 step, gated norm + out_proj; the steps exchange values stored with a tag "
+                    "that the readers poll; weights and state prefetched while waiting"}
 
 
 def density_field_bench(torch, dev, iters):

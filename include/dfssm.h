@@ -399,10 +399,9 @@ dfssm_status dfssm_decode_layers(const dfssm_decode_layer_weights* w, int64_t n_
  * dfssm_decode_layers_workspace_bytes() bytes per GPU (a file-scope device array, held
  * until the process ends; zeroed on `stream` the first time a device is used) serves
  * instead, so nothing is allocated or freed.  The array's size covers the largest stack
- * the call accepts
- * (n_layers <= 64; larger is DFSSM_ERR_INVALID_ARG).  Every call on one GPU shares that
- * GPU's array: calls that overlap on one GPU (other streams, other threads) race, so
- * the caller serializes them (one stream does).  DFSSM_ERR_HIP if the array's device
+ * the call accepts (n_layers <= 64; larger is DFSSM_ERR_INVALID_ARG).  Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race, so the caller serializes them (one stream does).  DFSSM_ERR_HIP if the array's device
  * address cannot be obtained.
  */
 dfssm_status dfssm_decode_layers_noalloc(const dfssm_decode_layer_weights* w, int64_t n_layers,
