@@ -151,10 +151,76 @@ __device__ bool read_pair(const Args& a, __amdgpu_buffer_rsrc_t r, int off, uint
     return ok;
 }
 
+// ---- cross-lane sums and maxima on the DPP paths: each step reads another lane's
+// register inside the VALU instruction (a ds_bpermute round trip through the LDS
+// crossbar costs ~100 cycles; the kernel's critical path runs ~45 such steps a layer).
+// The patterns are fixed, so every group forms the same float sum bit for bit.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowRor8 = 0x128;    // row_ror:8 (lane i <- lane i ^ 8 within a row of 16)
+constexpr int kDppMirror = 0x140;     // row_mirror (lane i <- lane 15 - i)
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror (lane i <- lane 7 - i within 8)
+constexpr int kDppBcast15 = 0x142;    // row_bcast:15 (rows 1, 3 <- lane 15 of the row before)
+constexpr int kDppBcast31 = 0x143;    // row_bcast:31 (rows 2, 3 <- lane 31)
+
+// Another lane's value (rows outside kRowMask get `identity`).
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ int dpp_i(int v, int identity = 0) {
+    return __builtin_amdgcn_update_dpp(identity, v, kCtrl, kRowMask, 0xF, false);
+}
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, false));
+}
+
+// Sum over each group of 8 lanes (every lane of the 8 gets it).
+__device__ __forceinline__ int32_t sum8(int32_t v) {
+    v += dpp_i<kDppXor1>(v);
+    v += dpp_i<kDppXor2>(v);
+    v += dpp_i<kDppHalfMirror>(v);
+    return v;
+}
+// Sums over each half-wave of 32 lanes: lanes 16..31 get lanes 0..31's, 48..63 get
+// 32..63's (T: int32_t or float; float sums in one fixed order).
+__device__ __forceinline__ int32_t sum32_hi(int32_t v) {
+    v = sum8(v);
+    v += dpp_i<kDppMirror>(v);
+    v += dpp_i<kDppBcast15, 0xA>(v);
+    return v;
+}
+__device__ __forceinline__ float sum32_hi(float v) {
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
+    v += dpp_f<kDppBcast15, 0xA>(v);
+    return v;
+}
+// The wave's sum or maximum (of non-negative values), uniform.
+__device__ __forceinline__ int32_t wave_sum_dpp(int32_t v) {
+    v = sum32_hi(v);
+    v += dpp_i<kDppBcast31, 0xC>(v);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v = sum32_hi(v);
+    v += dpp_f<kDppBcast31, 0xC>(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_absmax_dpp(float v) {  // v >= 0
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppMirror>(v));
+    v = fmaxf(v, dpp_f<kDppBcast15, 0xA>(v));
+    v = fmaxf(v, dpp_f<kDppBcast31, 0xC>(v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Maximum over the group (every thread gets it): one barrier; `red` is not reused
 // before a later barrier.
 __device__ __forceinline__ float group_max(float v, float* red) {
-    v = wave_max(v);
+    v = wave_absmax_dpp(v);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
     lds_barrier();
     float m = red[0];
@@ -166,7 +232,7 @@ __device__ __forceinline__ float group_max(float v, float* red) {
 // Sum over the group in one fixed order (a butterfly within each wave, then the waves
 // in order), so every group that sums the same values gets the same bits.
 __device__ __forceinline__ float group_sum_fixed(float v, float* red) {
-    for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+    v = wave_sum_dpp(v);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
     lds_barrier();
     float s = red[0];
@@ -219,7 +285,7 @@ struct Lds {
     __attribute__((aligned(16))) uint32_t planes[kDInner / 32 / 8 * kPlaneRow];  // plane order
     float red_max[kWaves], red_ss[kWaves];
     int32_t red_xsum[4];
-    int32_t rowred[kWaves][8];      // out_proj: per-wave partial sums of the group's 8 rows
+    int32_t rowred[kWaves][4][8];   // out_proj: per-(wave, 16-lane row) sums of the group's 8 rows
     int32_t tsl[kRank];             // t
     float xs[16], ys[16], Bs[kDState], Cs[kDState];
     float dt_h;
@@ -255,7 +321,7 @@ __device__ __forceinline__ void build_planes(Lds& s, int n_blocks) {
         int32_t part = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) part = byte_sum(nw[e], part);
-        part = wave_sum(part);
+        part = wave_sum_dpp(part);
         if ((threadIdx.x & (kWave - 1)) == 0) s.red_xsum[threadIdx.x / kWave] = part;
     }
 }
@@ -357,9 +423,8 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
                 acc = __builtin_amdgcn_sdot4((int)wbA[e].z, (int)c.z, acc, false);
                 acc = __builtin_amdgcn_sdot4((int)wbA[e].w, (int)c.w, acc, false);
             }
-#pragma unroll
-            for (int o = 16; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 32);
-            if (ks == 0) s.tsl[tr] = acc;
+            acc = sum32_hi(acc);
+            if (ks == 31) s.tsl[tr] = acc;
         }
         build_planes(s, kDModel / 32);
         if (a.trace && g == 0) {
@@ -378,8 +443,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) plane_dot_lds(wsA[i], s, 8 * kc + i, pa);
             int32_t S = plane_combine(pa);
-#pragma unroll
-            for (int o = 4; o > 0; o >>= 1) S += __shfl_xor(S, o, 8);
+            S = sum8(S);
             if (kc == 0 && a_live) {
                 const int32_t acc = 2 * S - s.red_xsum[0];
                 float lora = 0.0f;
@@ -457,11 +521,10 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
             acc = fmaf(hv.y, cc[1], acc);
             acc = fmaf(hv.z, cc[2], acc);
             acc = fmaf(hv.w, cc[3], acc);
-#pragma unroll
-            for (int o = 16; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 32);
+            acc = sum32_hi(acc);
             // y of channel sp goes through LDS to thread sp, which holds its z, gates it
             // and stores g
-            if (sq == 0) s.ys[sp] = fmaf(dph, xp, acc);
+            if (sq == 31) s.ys[sp] = fmaf(dph, xp, acc);
             lds_barrier();
             if (tid < 16) {
                 const float gv = s.ys[tid] * silu(zv);
@@ -540,9 +603,8 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
                 acc = __builtin_amdgcn_sdot4((int)wbC[e].z, (int)c.z, acc, false);
                 acc = __builtin_amdgcn_sdot4((int)wbC[e].w, (int)c.w, acc, false);
             }
-#pragma unroll
-            for (int o = 16; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 32);
-            if (ks == 0) s.tsl[tr] = acc;
+            acc = sum32_hi(acc);
+            if (ks == 31) s.tsl[tr] = acc;
         }
         build_planes(s, kDInner / 32);
         if (a.trace && g == 0) {
@@ -553,23 +615,24 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(Args a) {
         }
         lds_barrier();
         if (a.trace && g == 0 && tid < kRank) a.trace[(int64_t)l * kTrWords + kTrTOut + tid] = (uint32_t)s.tsl[tid];
-        // row 8 g + crow: 64 k per thread (blocks 2 cks, 2 cks + 1), summed over the 8
-        // slices of the wave (lanes crow + 8 i) and then over the 8 waves
+        // row 8 g + crow: 64 k per thread (blocks 2 cks, 2 cks + 1), summed over the 2
+        // slices of each 16-lane row (lanes crow, crow + 8), then through LDS over the
+        // 4 rows of each of the 8 waves
         {
             int32_t pa[4] = {0, 0, 0, 0};
             plane_dot_lds(wbitsC.x, s, 2 * cks, pa);
             plane_dot_lds(wbitsC.y, s, 2 * cks + 1, pa);
             int32_t S = plane_combine(pa);
-            S += __shfl_xor(S, 8, kWave);
-            S += __shfl_xor(S, 16, kWave);
-            S += __shfl_xor(S, 32, kWave);
-            if (lane < 8) s.rowred[wave][lane] = S;
+            S += dpp_i<kDppRowRor8>(S);
+            if ((lane & 15) < 8) s.rowred[wave][lane >> 4][lane & 7] = S;
         }
         lds_barrier();
         if (tid < 8) {
             int32_t S = 0;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) S += s.rowred[w][tid];
+            for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) S += s.rowred[w][q][tid];
             const int32_t acc = 2 * S - (s.red_xsum[0] + s.red_xsum[1]);
             float lora = 0.0f;
             const uint32_t words[4] = {waC.x, waC.y, waC.z, waC.w};
