@@ -10,8 +10,9 @@ that stage:
     their terms (the projection tests' bar);
   * Mamba-2 step: windows bit-exact, state and output within the step tests' bar.
 The last layer's output must equal x_out byte for byte, and a second token (the
-windows swapped, the state carried) must pass the same checks: the counters that the
-first call left behind were reset.
+windows swapped, the state carried) must pass the same checks: what the first call
+left in the workspace (the done count cleared, the call counter advanced, its tagged
+values) does not disturb the second.
 """
 import numpy as np
 import pytest

@@ -1,13 +1,14 @@
 """The no-allocation decode entry point (dfssm_decode_layers_noalloc) against the
 workspace form (dfssm_decode_layers), through the C ABI.
 
-Both run the same kernel; the only difference is where the counters and exchange
-slots live (the library's own per-GPU array instead of the caller's workspace).  Two
-calls in a row on the library's array, the second with a smaller stack (4 layers,
-then 2), must each reproduce the workspace form's outputs byte for byte: the last
-layer's output, every layer's trace, the advanced windows and the updated state, with
-a clear status word.  The second call also shows that the first left the shared
-array's counters cleared.
+Both run the same kernel; the only difference is where the done count, the call
+counter and the tagged exchange slots live (the library's own per-GPU array instead of
+the caller's workspace).  Two calls in a row on the library's array, the second with a
+smaller stack (4 layers, then 2), must each reproduce the workspace form's outputs
+byte for byte: the last layer's output, every layer's trace, the advanced windows and
+the updated state, with a clear status word.  The second call also shows that what
+the first left in the shared array (its done count cleared, its call counter
+advanced, its tagged values) does not disturb the next.
 """
 import numpy as np
 import pytest
