@@ -151,27 +151,9 @@ __device__ bool read_pair(const Args& a, __amdgpu_buffer_rsrc_t r, int off, uint
     return ok;
 }
 
-// ---- cross-lane sums and maxima on the DPP paths: each step reads another lane's
-// register inside the VALU instruction (a ds_bpermute round trip through the LDS
-// crossbar costs ~100 cycles; the kernel's critical path runs ~45 such steps a layer).
-// The patterns are fixed, so every group forms the same float sum bit for bit.
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
-constexpr int kDppRowRor8 = 0x128;    // row_ror:8 (lane i <- lane i ^ 8 within a row of 16)
-constexpr int kDppMirror = 0x140;     // row_mirror (lane i <- lane 15 - i)
-constexpr int kDppHalfMirror = 0x141; // row_half_mirror (lane i <- lane 7 - i within 8)
-constexpr int kDppBcast15 = 0x142;    // row_bcast:15 (rows 1, 3 <- lane 15 of the row before)
-constexpr int kDppBcast31 = 0x143;    // row_bcast:31 (rows 2, 3 <- lane 31)
-
-// Another lane's value (rows outside kRowMask get `identity`).
-template <int kCtrl, int kRowMask = 0xF>
-__device__ __forceinline__ int dpp_i(int v, int identity = 0) {
-    return __builtin_amdgcn_update_dpp(identity, v, kCtrl, kRowMask, 0xF, false);
-}
-template <int kCtrl, int kRowMask = 0xF>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, false));
-}
+// ---- cross-lane sums on the DPP paths (the helpers in device_common.h): the kernel's
+// critical path runs ~45 such steps a layer.  The patterns are fixed, so every group
+// forms the same float sums bit for bit.
 
 // Sum over each group of 8 lanes (every lane of the 8 gets it).
 __device__ __forceinline__ int32_t sum8(int32_t v) {
@@ -196,31 +178,17 @@ __device__ __forceinline__ float sum32_hi(float v) {
     v += dpp_f<kDppBcast15, 0xA>(v);
     return v;
 }
-// The wave's sum or maximum (of non-negative values), uniform.
-__device__ __forceinline__ int32_t wave_sum_dpp(int32_t v) {
-    v = sum32_hi(v);
-    v += dpp_i<kDppBcast31, 0xC>(v);
-    return __builtin_amdgcn_readlane(v, 63);
-}
-__device__ __forceinline__ float wave_sum_dpp(float v) {
+// The wave's float sum in one fixed order, uniform.
+__device__ __forceinline__ float wave_sum_fixed(float v) {
     v = sum32_hi(v);
     v += dpp_f<kDppBcast31, 0xC>(v);
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-__device__ __forceinline__ float wave_absmax_dpp(float v) {  // v >= 0
-    v = fmaxf(v, dpp_f<kDppXor1>(v));
-    v = fmaxf(v, dpp_f<kDppXor2>(v));
-    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
-    v = fmaxf(v, dpp_f<kDppMirror>(v));
-    v = fmaxf(v, dpp_f<kDppBcast15, 0xA>(v));
-    v = fmaxf(v, dpp_f<kDppBcast31, 0xC>(v));
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Maximum over the group (every thread gets it): one barrier; `red` is not reused
 // before a later barrier.
 __device__ __forceinline__ float group_max(float v, float* red) {
-    v = wave_absmax_dpp(v);
+    v = wave_max(v);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
     lds_barrier();
     float m = red[0];
@@ -232,7 +200,7 @@ __device__ __forceinline__ float group_max(float v, float* red) {
 // Sum over the group in one fixed order (a butterfly within each wave, then the waves
 // in order), so every group that sums the same values gets the same bits.
 __device__ __forceinline__ float group_sum_fixed(float v, float* red) {
-    v = wave_sum_dpp(v);
+    v = wave_sum_fixed(v);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
     lds_barrier();
     float s = red[0];
@@ -321,7 +289,7 @@ __device__ __forceinline__ void build_planes(Lds& s, int n_blocks) {
         int32_t part = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) part = byte_sum(nw[e], part);
-        part = wave_sum_dpp(part);
+        part = wave_sum(part);
         if ((threadIdx.x & (kWave - 1)) == 0) s.red_xsum[threadIdx.x / kWave] = part;
     }
 }

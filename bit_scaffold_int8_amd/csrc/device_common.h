@@ -142,14 +142,49 @@ __device__ __forceinline__ int32_t opaque_one() {
     return one;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+// ---- cross-lane steps on the DPP paths: each reads another lane's register inside a
+// VALU instruction (a shuffle through ds_bpermute is an LDS round trip, ~100 cycles).
+// Every lane of the wave must be active.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowRor8 = 0x128;    // row_ror:8 (lane i <- lane i ^ 8 within a row of 16)
+constexpr int kDppMirror = 0x140;     // row_mirror (lane i <- lane 15 - i)
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror (lane i <- lane 7 - i within 8)
+constexpr int kDppBcast15 = 0x142;    // row_bcast:15 (rows 1, 3 <- lane 15 of the row before)
+constexpr int kDppBcast31 = 0x143;    // row_bcast:31 (rows 2, 3 <- lane 31)
+
+// Another lane's value; rows outside kRowMask get `identity`.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ int dpp_i(int v, int identity = 0) {
+    return __builtin_amdgcn_update_dpp(identity, v, kCtrl, kRowMask, 0xF, false);
+}
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ float dpp_f(float v, float identity = 0.0f) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v), kCtrl, kRowMask, 0xF, false));
 }
 
+// The wave's maximum, in every lane (exact: any order gives the same value).
+__device__ __forceinline__ float wave_max(float v) {
+    const float lo = -__builtin_inff();
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppMirror>(v));
+    v = fmaxf(v, dpp_f<kDppBcast15, 0xA>(v, lo));
+    v = fmaxf(v, dpp_f<kDppBcast31, 0xC>(v, lo));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// The wave's integer sum, in every lane.
 __device__ __forceinline__ int32_t wave_sum(int32_t v) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v += dpp_i<kDppXor1>(v);
+    v += dpp_i<kDppXor2>(v);
+    v += dpp_i<kDppHalfMirror>(v);
+    v += dpp_i<kDppMirror>(v);
+    v += dpp_i<kDppBcast15, 0xA>(v);
+    v += dpp_i<kDppBcast31, 0xC>(v);
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 }  // namespace dfssm
