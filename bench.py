@@ -305,7 +305,9 @@ def parse():
     ap.add_argument("--no-sweeps", action="store_true",
                     help="skip the launch-heavy legs (per-call graphs, 48-layer sweep and chain): counter "
                          "runs, where every dispatch is serialized")
-    ap.add_argument("--prefill-iters", type=int, default=10)
+    ap.add_argument("--prefill-iters", type=int, default=50)
+    ap.add_argument("--prefill-settle-seconds", type=float, default=0.3,
+                    help="each prefill call runs back to back this long before it is timed")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the GEMV traffic record from two rocprofv3 counter_collection.csv files")
     ap.add_argument("--util-from", metavar="COUNTER_CSV",
@@ -337,6 +339,16 @@ def time_events(torch, fn, iters, stream):
     e.record(stream)
     e.synchronize()
     return s.elapsed_time(e) / iters
+
+
+def settle_for(torch, fn, seconds, stream):
+    """fn() back to back for about `seconds` (the clocks reach their loaded state), then
+    wait for the stream."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        stream.synchronize()
 
 
 def decode_batched(torch, dp, stream, steps, warmup):
@@ -915,13 +927,16 @@ def main():
             pp.forward_contract(debug=False)
             pp.forward(debug=False)
             torch.cuda.synchronize()
-            # settle, then the specified call (t = W_B x_q inside the product), the
-            # quantizer before it, and the split form (t from quantize_lora_down)
-            time_events(torch, lambda: pp.gemm_computing_t(stream, debug=False), 20, stream)
-            g_ms = time_events(torch, lambda: pp.gemm_computing_t(stream, debug=False), args.prefill_iters, stream)
-            qa_ms = time_events(torch, lambda: pp.quantize(stream), args.prefill_iters, stream)
-            q_ms = time_events(torch, lambda: pp.quantize_lora_down(stream), args.prefill_iters, stream)
-            gt_ms = time_events(torch, lambda: pp.gemm(stream, debug=False), args.prefill_iters, stream)
+            # the specified call (t = W_B x_q inside the product), the quantizer before
+            # it, and the split form (t from quantize_lora_down), each timed after it
+            # ran back to back for a while (steady clocks, as under sustained prefill)
+            def timed(fn):
+                settle_for(torch, fn, args.prefill_settle_seconds, stream)
+                return time_events(torch, fn, args.prefill_iters, stream)
+            g_ms = timed(lambda: pp.gemm_computing_t(stream, debug=False))
+            qa_ms = timed(lambda: pp.quantize(stream))
+            q_ms = timed(lambda: pp.quantize_lora_down(stream))
+            gt_ms = timed(lambda: pp.gemm(stream, debug=False))
             tops = gemm_ops(pM, pN, pK) / (g_ms * 1e-3) / 1e12
             pre[name] = {"M": pM, "K": pK, "N": pN, "gemm_us": round(g_ms * 1e3, 2),
                          "quantize_us": round(qa_ms * 1e3, 2), "TOPS": round(tops, 1),

@@ -190,36 +190,33 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     uint8_t* const bbuf = abuf + 2 * C::kABytes;       // 2 x kBBytes
     int32_t* const rowsum = reinterpret_cast<int32_t*>(lds + C::kRowSumOff);
 
-    // code staging: piece j -> row j GS / 8 + tg / 8, bytes [16 p, +16)
+    // code staging: piece j -> row j GS / 8 + tg / 8, bytes [16 p, +16).  One base
+    // offset per lane (piece j adds a uniform j GS / 8 rows): rows past `rows` lie past
+    // the end of a_rsrc and read zero, so no per-piece offsets stay live in registers.
     const int p16 = 16 * (tg & 7);
-    int st_goff[P], st_loff[P];
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-        const int r = j * (GS / 8) + (tg >> 3);
-        st_goff[j] = r < rows ? r * K + p16 : kLoadDead;
-        st_loff[j] = r * kLdA + p16;
-    }
-    // sign staging: slot i -> group column (tg / 4) + (GS / 4) i, chunk (tg & 3) of the block
-    int bs_goff[JB], bs_loff[JB];
-#pragma unroll
-    for (int i = 0; i < JB; ++i) {
-        const int c = (tg >> 2) + (GS / 4) * i;
-        bs_goff[i] = c < cols_g ? c * RB + 16 * (tg & 3) : kLoadDead;
-        bs_loff[i] = c * kLdB + 16 * (tg & 3);
-    }
+    const int st_gbase = (tg >> 3) * K + p16;
+    const int st_lbase = (tg >> 3) * kLdA + p16;
+    // sign staging: slot i -> group column (tg / 4) + (GS / 4) i, chunk (tg & 3) of the
+    // block (columns past cols_g lie past the end of b_rsrc)
+    const int bs_gbase = (tg >> 2) * RB + 16 * (tg & 3);
+    const int bs_lbase = (tg >> 2) * kLdB + 16 * (tg & 3);
+    auto st_loff = [&](int j) { return st_lbase + j * (GS / 8) * kLdA; };
+    auto bs_loff = [&](int i) { return bs_lbase + i * (GS / 4) * kLdB; };
 
     auto st_load = [&](int c, int j) -> v4i {
         const int k = c * kChunk;
         const bool live = c < c_end && k + p16 < K;
         return __builtin_bit_cast(
-            v4i, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, live ? st_goff[j] + k : kLoadDead, 0, 0));
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, live ? st_gbase + (j * (GS / 8) * K + k) : kLoadDead,
+                                                       0, 0));
     };
     // sign bits of block b (chunks c_begin + 4 b .. + 3), slot i: 16 bytes of its chunk
     auto bs_load = [&](int b, int i) -> v4i {
         const int c0 = c_begin + kBlk * b;
         const bool live = b < nblk && c0 + (tg & 3) < c_end;
         return __builtin_bit_cast(
-            v4i, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, live ? bs_goff[i] + 16 * c0 : kLoadDead, 0, 0));
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                     b_rsrc, live ? bs_gbase + (i * (GS / 4) * RB + 16 * c0) : kLoadDead, 0, 0));
     };
     // A operand of step s, row block mb: row 32 mb + l32, bytes [64 g + 16 s, +16)
     auto a_frag = [&](int buf, int s, int mb) -> v4i {
@@ -273,13 +270,13 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     if constexpr (kTin) wbv = wb_load(c_begin, 0);
 #pragma unroll
     for (int j = 0; j < P; ++j) {
-        *reinterpret_cast<v4i*>(abuf + st_loff[j]) = stage[j];
+        *reinterpret_cast<v4i*>(abuf + st_loff(j)) = stage[j];
 #pragma unroll
         for (int w = 0; w < 4; ++w) rsum[j] = byte_sum((uint32_t)stage[j][w], rsum[j]);
         stage[j] = st_load(c_begin + 1, j);
     }
 #pragma unroll
-    for (int i = 0; i < JB; ++i) *reinterpret_cast<v4i*>(bbuf + bs_loff[i]) = bst[i];
+    for (int i = 0; i < JB; ++i) *reinterpret_cast<v4i*>(bbuf + bs_loff(i)) = bst[i];
     lds_barrier();
     v4i afr[2][MB], bop[2][NB];
     v2u bits0[NB], bits1[NB];
@@ -319,7 +316,7 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
 #pragma unroll
             for (int j = 0; j < P; ++j) {
                 if (st_step(j) != s) continue;
-                *reinterpret_cast<v4i*>(abuf + nxt * C::kABytes + st_loff[j]) = stage[j];
+                *reinterpret_cast<v4i*>(abuf + nxt * C::kABytes + st_loff(j)) = stage[j];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) rsum[j] = byte_sum((uint32_t)stage[j][w], rsum[j]);
                 stage[j] = st_load(c + 2, j);
@@ -341,7 +338,7 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
                 if (q == 2) {
 #pragma unroll
                     for (int i = 0; i < JB; ++i)
-                        *reinterpret_cast<v4i*>(bbuf + (bb_cur ^ 1) * C::kBBytes + bs_loff[i]) = bst[i];
+                        *reinterpret_cast<v4i*>(bbuf + (bb_cur ^ 1) * C::kBBytes + bs_loff(i)) = bst[i];
                 }
                 lds_barrier();
             }
