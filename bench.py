@@ -703,8 +703,9 @@ def lm_head_decode(torch, dev, stream, steps, warmup):
             dfssm.dfssm_int8_rowscale_gemm(x_q, s_x, e[0], s_e[0], y, None, stream)
         for _ in range(warmup):
             cold()
-        torch.cuda.synchronize()
+        settle_for(torch, cold, 0.2, stream)
         cold_ms = time_events(torch, cold, 3 * steps, stream)
+        settle_for(torch, warm, 0.1, stream)
         warm_ms = time_events(torch, warm, steps, stream)
         b = head_bytes(M, N, K)
         out[f"M{M}"] = {"cold_us": round(cold_ms * 1e3, 2), "cold_GBps": round(b / (cold_ms * 1e-3) / 1e9, 1),

@@ -20,15 +20,16 @@
 //  * rows go in stages of T tiles, loaded through a buffer resource two stages ahead
 //    into three register buffers that rotate by name; the waves' partial sums meet in
 //    LDS (atomics from the token lanes), double-buffered by stage parity so one
-//    barrier per stage suffices; the epilogue scales and stores through buffer
-//    resources with out-of-range offsets for dead elements.
+//    barrier per stage suffices; the epilogue scales each stage's outputs into LDS,
+//    and the group writes its whole [M][rows] block of y once, after its last stage
+//    (small stores mixed into the weight stream slow the stream down).
 #include "device_common.h"
 
 namespace dfssm {
 
 constexpr int kHeadWaves = 8;
 constexpr int kHeadThreads = kHeadWaves * kWave;
-constexpr int kHeadRowsCap = 2048;  // rows one group owns at most (their scales live in LDS)
+constexpr int kHeadRowsCap = 512;  // rows one group owns at most (their scales and y live in LDS)
 
 // C 16-byte pieces per lane per row, T 16-row tiles per stage.
 template <int C, int T>
@@ -42,6 +43,7 @@ __global__ __launch_bounds__(kHeadThreads) void int8_gemv_kernel(
     constexpr int E = (16 + kTokStride - 1) / kTokStride;  // tokens per epilogue thread
 
     __shared__ float se_lds[kHeadRowsCap];
+    __shared__ float y_lds[16][kHeadRowsCap];  // [token][row of the group]
     // row stride 20 words: the adds of one instruction (rows 4g+v, tokens i) hit
     // distinct banks
     __shared__ int32_t red[2][T * 16][20];
@@ -112,7 +114,6 @@ __global__ __launch_bounds__(kHeadThreads) void int8_gemv_kernel(
     for (int q = threadIdx.x; q < 2 * T * 16 * 20; q += NT) (&red[0][0][0])[q] = 0;
     lds_barrier();
 
-    const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(y, (uint32_t)(M * N * 4));
     const __amdgpu_buffer_rsrc_t acc_rsrc = make_rsrc(acc_dbg, acc_dbg ? (uint32_t)(M * N * 4) : 0u);
     const int erow = threadIdx.x % (T * 16);
     const int etok0 = threadIdx.x / (T * 16);
@@ -143,9 +144,8 @@ __global__ __launch_bounds__(kHeadThreads) void int8_gemv_kernel(
             if (tok < M) {
                 const int32_t a = red[rb][erow][tok];
                 red[rb][erow][tok] = 0;  // ready for the stage after next
-                const int off = n < N ? (int)(((int64_t)tok * N + n) * 4) : kOffDead;
-                store_f32(sxs[tok] * (se * (float)a), y_rsrc, off);
-                store_i32(a, acc_rsrc, off);
+                y_lds[tok][n - row0] = sxs[tok] * (se * (float)a);
+                if (acc_dbg) store_i32(a, acc_rsrc, n < N ? (int)(((int64_t)tok * N + n) * 4) : kOffDead);
             }
         }
         // no second barrier: the next stage adds into the other buffer, and this one is
@@ -156,6 +156,15 @@ __global__ __launch_bounds__(kHeadThreads) void int8_gemv_kernel(
         run_stage(st, s0, s2, rb);
         run_stage(st + 1, s1, s0, rb ^ 1);
         run_stage(st + 2, s2, s1, rb);
+    }
+    // the group's y: token by token, its rows below N, consecutive threads on
+    // consecutive rows (one coalesced run per token)
+    lds_barrier();
+    const int live_rows = (int)(N - row0 < nrows ? N - row0 : nrows);
+    const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(y + row0, (uint32_t)((M - 1) * N * 4 + live_rows * 4));
+    for (int q = threadIdx.x; q < M * live_rows; q += NT) {
+        const int tok = q / live_rows, r = q - tok * live_rows;
+        store_f32(y_lds[tok][r], y_rsrc, (int)(((int64_t)tok * N + r) * 4));
     }
 }
 
