@@ -52,6 +52,14 @@ class DfssmError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bit_scaffold_int8_amd.build`")
+    # torch ships its own HIP runtime and loads it by path.  Loaded first, the library
+    # would bring in the system's copy as well, and device pointers from torch would not
+    # be valid in the library's runtime; with torch loaded first, the library's
+    # dependency resolves to torch's runtime (same soname).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.dfssm_status_string.argtypes = [ctypes.c_int]

@@ -328,3 +328,15 @@ def _decode_layers(**kw):
 ])
 def test_decode_layers_rejects(kw, want):
     assert _decode_layers(**kw) == want
+
+
+def test_binding_shares_torchs_hip_runtime():
+    # importing the binding before torch must leave one HIP runtime in the process (two
+    # would make torch's device pointers invalid in the library's launches)
+    import subprocess
+    import sys
+    code = ("import bit_scaffold_int8_amd.dfssm, torch; "
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}; print(len(paths))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip() == "1", out.stdout
