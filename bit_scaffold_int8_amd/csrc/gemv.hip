@@ -140,6 +140,12 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
         }
     }
 
+    // Issue priority.  A SIMD issues from its highest-priority wave first, then the
+    // oldest, so of two groups sharing a CU the younger one falls behind from its setup
+    // on and ends its stream alone.  The setup runs at the top priority, and in the
+    // stream a group's priority steps down with each quarter of its stages, so the group
+    // that lags issues first until the two are level.
+    __builtin_amdgcn_s_setprio(3);
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int i = lane & 15;
@@ -702,6 +708,13 @@ __attribute__((amdgpu_waves_per_eu(C == 1 && (W == 8 || (W == 4 && (T == 1 || kS
 
     // three stages per trip so the register buffers rotate by name
     for (int64_t st = st_begin; st < st_end; st += 3) {
+        {
+            const int64_t done4 = 4 * (st - st_begin), n = st_end - st_begin;  // uniform
+            if (done4 < n) __builtin_amdgcn_s_setprio(3);
+            else if (done4 < 2 * n) __builtin_amdgcn_s_setprio(2);
+            else if (done4 < 3 * n) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
         const int rb = (int)((st - st_begin) & 1);
         run_stage(st, s0, s2, rb);
         run_stage(st + 1, s1, s0, rb ^ 1);
