@@ -641,9 +641,7 @@ def density_field_bench(torch, dev, iters):
     }
     res = {"rows": R, "d_state": d, "field_bytes_per_row": d // 8 * 4 + 4, "state_bytes_per_row": 4 * d}
     for name, (fn, per_row) in legs.items():
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
+        settle_for(torch, fn, 0.1, stream)
         ms = time_events(torch, fn, iters, stream)
         res[name] = {"us": round(ms * 1e3, 2), "GBps": round(R * per_row / (ms * 1e-3) / 1e9, 1),
                      "frac_of_hbm_peak": round(R * per_row / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}

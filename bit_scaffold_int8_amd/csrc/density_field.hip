@@ -31,8 +31,11 @@ namespace {
 constexpr int kDfRows = 64;       // rows per encode group, one per thread
 constexpr int kDfDecThreads = 256;
 
+// Rows of up to 128 values: three waves per SIMD (at most 168 registers, a few values
+// spilled outside the chain) hide the chain's dependent steps and hazard waits better
+// than two: encode 47.3 -> 46.3 us, round trip 65.0 -> 61.0 us for 262144 rows of 128.
 template <int D>
-__global__ __launch_bounds__(kDfRows) void density_encode_kernel(const float* __restrict__ state, int64_t R,
+__global__ __launch_bounds__(kDfRows) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 3 : 1, D <= 128 ? 3 : 8))) void density_encode_kernel(const float* __restrict__ state, int64_t R,
                                                                   uint32_t* __restrict__ field,
                                                                   float* __restrict__ scale,
                                                                   float* __restrict__ state_out) {
