@@ -74,7 +74,12 @@ struct Cfg {
     static constexpr int GS = kWave * WNW;                   // threads of one K group
     static constexpr int P = BM * 8 / GS;                    // code pieces per thread per chunk
     static constexpr int JB = BN * kBlk / GS;                // sign pieces per thread per block
-    static constexpr int kABytes = BM * kLdA, kBBytes = BN * kLdB;
+    // The narrow configurations (at most 2 accumulator blocks per wave) stage W_B with
+    // the codes in the instances that compute t; a code chunk buffer then holds BM token
+    // rows and after them the chunk's kRank rows of W_B.  (The wider ones lack the
+    // registers, or, at 4 blocks, measured slower with the extra LDS traffic.)
+    static constexpr bool kStageWb = MB * NB <= 2;
+    static constexpr int kABytes = (BM + (kStageWb ? kRank : 0)) * kLdA, kBBytes = BN * kLdB;
     static constexpr int kGroupBytes = 2 * kABytes + 2 * kBBytes;
     static constexpr int RBLK = MB * NB < kRedBlocks ? MB * NB : kRedBlocks;  // blocks per hand-over phase
     static constexpr int kRedBytes = KS > 1 ? WNW * RBLK * KS * 4 * kWave * 16 : 0;
@@ -86,6 +91,7 @@ struct Cfg {
     static_assert(KS == 1 || KS == 2 || KS == 4, "waves split over K and N");
     static_assert(P * GS == BM * 8 && (P % 4 == 0 || 4 % P == 0), "code pieces split evenly over steps");
     static_assert(JB * GS == BN * kBlk, "sign pieces split evenly over threads");
+    static_assert(!kStageWb || GS >= 8 * kRank, "a K group has a thread for each W_B piece of a chunk");
     static_assert(kLdsBytes * OCC <= 160 * 1024, "LDS");
 };
 
@@ -141,7 +147,7 @@ __device__ __forceinline__ v8bf pack_bf16(const uint32_t (&b)[8]) {
 
 // One output tile of configuration C over the column range of `seg`.  kTin: the LoRA
 // down-projection t = W_B x_q is computed here, from the code chunks already in LDS, on
-// v_mfma_i32_16x16x64_i8 (A = 16 token rows, B = the 16 rows of W_B read from memory):
+// v_mfma_i32_16x16x64_i8 (A = 16 token rows, B = the 16 rows of W_B):
 // the waves of a K group share the tile's 16-row blocks, and the K groups' partial t
 // meet in LDS after the main loop.
 template <class C, bool kDebug, bool kTin>
@@ -230,8 +236,17 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     };
     auto b_op = [](const v2u& bits, int s) -> v4i { return bits16((s < 2 ? bits.x : bits.y) >> (16 * (s & 1))); };
 
-    // kTin: W_B row (lane & 15) over k = c kChunk + 64 h + 16 (lane >> 4), h = 0, 1 (the
-    // B operand of the t MFMAs); chunks past the group's range or past K read zero
+    // kTin: W_B, the B operand of the t MFMAs (row lane & 15 over k = c kChunk + 64 h +
+    // 16 (lane >> 4) in k-step h = 0, 1).  Chunks past the group's range or past K read
+    // zero.  Two ways in:
+    //  * staged (kWbLds): the chunk's kRank rows (kRank x 128 bytes) travel with its
+    //    codes, two chunks ahead, by the K group's first 8 kRank threads (whole waves):
+    //    piece tg -> row tg / 8, bytes [p16, +16), after the buffer's BM code rows (the
+    //    code staging's base offsets serve).  The t MFMAs read them from LDS;
+    //  * loaded (the widest configurations, whose registers are spent): each k-step's
+    //    piece straight from memory a step or two ahead, one register set.  A wait for
+    //    it also waits for the staging loads issued before it, cutting their slack.
+    constexpr bool kWbLds = kTin && C::kStageWb;
     const bool lora = a.rank != 0;
     const __amdgpu_buffer_rsrc_t wb_rsrc = make_rsrc(a.w_b, (kTin && lora) ? (uint32_t)(kRank * K) : 0u);
     const int wb_lane = (lane & 15) * K + 16 * (lane >> 4);
@@ -240,6 +255,18 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
         const bool live = kTin && c < c_end && k < K;
         return __builtin_bit_cast(
             v4i, __builtin_amdgcn_raw_buffer_load_b128(wb_rsrc, live ? wb_lane + k : kLoadDead, 0, 0));
+    };
+    const bool wb_stager = tg < 8 * kRank;  // wave-uniform: whole waves
+    const int wb_loff = st_lbase + BM * kLdA;
+    auto wb_stage_load = [&](int c) -> v4i {
+        const int k = c * kChunk;
+        const bool live = kTin && wb_stager && c < c_end && k + p16 < K;
+        return __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(wb_rsrc, live ? st_gbase + k : kLoadDead, 0, 0));
+    };
+    auto wb_frag = [&](int buf, int h) -> v4i {
+        return *reinterpret_cast<const v4i*>(abuf + buf * C::kABytes + (BM + (lane & 15)) * kLdA + 64 * h +
+                                             16 * (lane >> 4));
     };
     // A operand of the t MFMAs: token rows 16 rb + (lane & 15) of block j, k-step h
     auto ta_frag = [&](int buf, int j, int h) -> v4i {
@@ -250,7 +277,7 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     v4i tacc[kTin ? TB : 1];
 #pragma unroll
     for (int j = 0; j < (kTin ? TB : 1); ++j) tacc[j] = (v4i){0, 0, 0, 0};
-    v4i wbv;  // the W_B piece of the next t k-step (one register set)
+    v4i wbv;  // loaded: the W_B piece of the next t k-step; staged: this thread's piece of the next chunk
 
     v16i acc[MB][NB];
 #pragma unroll
@@ -267,7 +294,8 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     for (int j = 0; j < P; ++j) stage[j] = st_load(c_begin, j);
 #pragma unroll
     for (int i = 0; i < JB; ++i) bst[i] = bs_load(0, i);
-    if constexpr (kTin) wbv = wb_load(c_begin, 0);
+    if constexpr (kWbLds) wbv = wb_stage_load(c_begin);
+    else if constexpr (kTin) wbv = wb_load(c_begin, 0);
 #pragma unroll
     for (int j = 0; j < P; ++j) {
         *reinterpret_cast<v4i*>(abuf + st_loff(j)) = stage[j];
@@ -277,6 +305,10 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     }
 #pragma unroll
     for (int i = 0; i < JB; ++i) *reinterpret_cast<v4i*>(bbuf + bs_loff(i)) = bst[i];
+    if constexpr (kWbLds) {
+        if (wb_stager) *reinterpret_cast<v4i*>(abuf + wb_loff) = wbv;
+        wbv = wb_stage_load(c_begin + 1);
+    }
     lds_barrier();
     v4i afr[2][MB], bop[2][NB];
     v2u bits0[NB], bits1[NB];
@@ -301,8 +333,9 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
     // barrier per chunk sits in step 3, after the last store and before the first read
     // of the next chunk; every read of the current buffers was issued before it.
     // kTin: the t MFMAs of k-step h run in step h, beside the main MFMAs, on the current
-    // code buffer; the W_B piece of k-step 1 is loaded in step 0, and the next chunk's
-    // first piece in step 2 (one register set).
+    // code buffer.  Staged W_B: step 0 stores the next chunk's piece and loads the one two
+    // chunks ahead, like a code piece.  Loaded W_B: the piece of k-step 1 is loaded in
+    // step 0, and the next chunk's first piece in step 2.
     auto chunk = [&](int b, int q, const v2u (&bc)[NB], v2u (&bn)[NB]) {
         const int c = c_begin + kBlk * b + q;
         const int cur = q & 1, nxt = cur ^ 1;
@@ -327,12 +360,20 @@ __device__ __forceinline__ void prefill_tile(const prefill::Args& a, uint8_t* __
             }
             if constexpr (kTin) {
                 if (s < 2) {
+                    const v4i wb = kWbLds ? wb_frag(cur, s) : wbv;
 #pragma unroll
                     for (int j = 0; j < TB; ++j)
-                        tacc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ta_frag(cur, j, s), wbv, tacc[j], 0, 0, 0);
+                        tacc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ta_frag(cur, j, s), wb, tacc[j], 0, 0, 0);
                 }
-                if (s == 0) wbv = wb_load(c, 1);
-                if (s == 2) wbv = wb_load(c + 1, 0);
+                if constexpr (kWbLds) {
+                    if (s == 0) {
+                        if (wb_stager) *reinterpret_cast<v4i*>(abuf + nxt * C::kABytes + wb_loff) = wbv;
+                        wbv = wb_stage_load(c + 2);
+                    }
+                } else {
+                    if (s == 0) wbv = wb_load(c, 1);
+                    if (s == 2) wbv = wb_load(c + 1, 0);
+                }
             }
             if (s == 3) {
                 if (q == 2) {
