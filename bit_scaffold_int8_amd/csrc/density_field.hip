@@ -17,8 +17,8 @@
 // The modulator is a chain over a row's cells, so a thread takes a whole row, held in
 // registers: a group of 64 threads stages its 64 rows through LDS 32 values at a time
 // with coalesced 16-byte loads (chunk stride 33 words, so each thread's copy of its own
-// row falls in distinct banks), computes the densities (independent divisions, ahead
-// of the chain), then runs the chain and writes its words.  A small tile keeps several
+// row falls in distinct banks), computes the densities (independent quotients by one
+// scale, ahead of the chain), then runs the chain and writes its words.  A small tile keeps several
 // groups resident per SIMD, so their chains overlap.  The
 // readout is one thread per word (eight popcounts, two 16-byte stores).  Both passes
 // are bound by HBM traffic (the state) at the sizes a decode batch holds.
@@ -86,11 +86,30 @@ __global__ __launch_bounds__(kDfRows) __attribute__((amdgpu_waves_per_eu(D <= 12
     float s = 0.0f;
 #pragma unroll
     for (int n = 0; n < D; ++n) s = fmaxf(s, fabsf(v[n]));
-    // densities, in place: independent divisions, ahead of the chain
+    // densities, in place: independent quotients, ahead of the chain.  Every value of
+    // the row is divided by the same s, so the correctly rounded quotient v / s costs
+    // one IEEE reciprocal per row and four operations per value (Markstein's
+    // correction on operands scaled by a power of two):
+    //   k = 1 - exponent(s), s' = s 2^k in [1, 2), v' = v 2^k  (exact scalings),
+    //   y = RN(1 / s'), q0 = RN(v' y), r = v' - q0 s' (exact, one FMA), q = RN(q0 + r y).
+    // With y within half an ulp of 1/s' and q0 within an ulp of v'/s' = v/s, q is
+    // RN(v / s) (Markstein's theorem).  Only where v' falls below the normal range can
+    // the scaling round, and there |v / s| < 2^-126, far below what moves (q + 1) / 2.
+    // s = 0 (an all-zero row) takes s' = 1 and k = 0 (q = 0); s = inf takes s' = 1 and
+    // k = -300, sending finite values to zero (v / inf = 0) and infinite ones to NaN.
+    {
+        const bool fin = s > 0.0f && s <= 0x1.fffffep127f;
+        const int k = fin ? 1 - __builtin_amdgcn_frexp_expf(s) : (s > 0.0f ? -300 : 0);
+        const float sp = fin ? __builtin_ldexpf(s, k) : 1.0f;
+        const float y = 1.0f / sp;  // IEEE division
 #pragma unroll
-    for (int n = 0; n < D; ++n) {
-        const float a = s > 0.0f ? v[n] / s : 0.0f;  // IEEE division
-        v[n] = (a + 1.0f) * 0.5f;                    // the halving is exact
+        for (int n = 0; n < D; ++n) {
+            const float vp = __builtin_ldexpf(v[n], k);
+            const float q0 = vp * y;
+            const float rr = __builtin_fmaf(-q0, sp, vp);
+            const float a = __builtin_fmaf(rr, y, q0);
+            v[n] = (a + 1.0f) * 0.5f;  // the halving is exact
+        }
     }
     // the modulator over the row's cells, 32 cells (8 values) per field word
     const int64_t r = r0 + (live ? tid : 0);

@@ -91,3 +91,44 @@ def test_density_field_full_decode_batch(torch_cuda):
     assert np.array_equal(field.cpu().numpy().view(np.uint32)[idx], f_ref)
     assert np.array_equal(scale.cpu().numpy()[idx].view(np.uint32), s_ref.view(np.uint32))
     assert np.array_equal(out.cpu().numpy()[idx].view(np.uint32), dfc.decode(f_ref, s_ref, d).view(np.uint32))
+
+
+def test_density_field_scales_across_the_fp32_range(torch_cuda):
+    # Row scales over the whole fp32 range: subnormal, tiny, normal, huge (up to the
+    # largest finite value) and infinite.  Within a row: the scale itself, values just
+    # below it, all-ones significands, values far below it (quotients that underflow)
+    # and exact dyadic ratios.  The encode forms v / s through a power-of-two scaling
+    # and a correction step; field, scale and readout must still be bit-exact.
+    rng = np.random.default_rng(11)
+    d = 128
+    rows = []
+    for e in list(range(-149, 128, 2)) + [127]:
+        m = np.float32(1) + rng.random(dtype=np.float32)
+        if e == 127:
+            m = np.float32(np.nextafter(np.float32(2), np.float32(0)))  # the largest finite scale
+        s = np.ldexp(m, e).astype(np.float32)
+        if not np.isfinite(s) or s == 0:
+            continue
+        frac = rng.uniform(-1, 1, d).astype(np.float32)
+        v = (s * frac).astype(np.float32)
+        v[0] = s
+        v[1] = -np.nextafter(s, np.float32(0))
+        v[2] = np.float32(np.uint32((s.view(np.uint32) & 0xFF800000) | 0x7FFFFF).view(np.float32))
+        v[3:11] = np.ldexp(np.float32(1) + rng.random(8, dtype=np.float32), e - rng.integers(20, 160, 8)).astype(np.float32)
+        v[11:19] = (s * (rng.integers(-64, 65, 8) / np.float32(64))).astype(np.float32)
+        v = np.clip(v, -s, s).astype(np.float32)
+        rows.append(v)
+    inf_row = rng.uniform(-1e3, 1e3, d).astype(np.float32)
+    inf_row[5] = np.inf
+    ninf_row = inf_row.copy()
+    ninf_row[5] = -np.inf
+    x = np.stack(rows + [inf_row, ninf_row, np.zeros(d, np.float32)]).astype(np.float32)
+    f_ref, s_ref = dfc.encode(x)
+    with np.errstate(invalid="ignore"):  # the infinite rows read out inf * 0 = NaN
+        v_ref = dfc.decode(f_ref, s_ref, d)
+    for mode in ("encode_decode", "requantize"):
+        f, s, v = _gpu(x, mode)
+        assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32)), f"{mode}: scale"
+        bad = np.nonzero((f != f_ref).any(axis=1))[0]
+        assert bad.size == 0, f"{mode}: field differs in rows {bad[:8]} (scales {s_ref[bad[:8]]})"
+        assert np.array_equal(v.view(np.uint32), v_ref.view(np.uint32)), f"{mode}: readout"
