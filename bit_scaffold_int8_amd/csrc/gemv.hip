@@ -780,16 +780,21 @@ static hipError_t launch_gemv_wct(bool fast, int setup, const int8_t* x_q, const
     const bool throughput = batch * num_stages >= 4 * resident_wgs;
     constexpr int kRowsCap = gemv_rows_cap(W, T);
     constexpr int64_t kMaxStages = kRowsCap / (T * 16);
+    // Groups per problem round down, so a launch never spills a few groups into a
+    // partial second round, nor puts a second group on a few CUs while the rest hold one
+    // (batch 48: in_proj 1056 groups for 1024 resident, out_proj one-call 288 groups on
+    // 256 CUs, when rounded up).
     int64_t per_problem;
     if (throughput) {
         // whole resident rounds: as few as the rows cap allows, their groups spread
         // evenly over the problems (and a problem's stages evenly over its groups)
         const int64_t rounds = (batch * num_stages + resident_wgs * kMaxStages - 1) / (resident_wgs * kMaxStages);
-        per_problem = (rounds * resident_wgs + batch - 1) / batch;
+        per_problem = (rounds * resident_wgs) / batch;
     } else {
         const int64_t target_wgs = setup != kGivenT ? 256 : 2048;
-        per_problem = (target_wgs + batch - 1) / batch;
+        per_problem = target_wgs / batch;
     }
+    if (per_problem < 1) per_problem = 1;
     const int64_t min_groups = (num_stages + kMaxStages - 1) / kMaxStages;  // the rows cap
     if (per_problem < min_groups) per_problem = min_groups;
     if (per_problem > num_stages) per_problem = num_stages;
