@@ -360,3 +360,35 @@ def test_quantizer_near_ties_bit_exact(torch_cuda):
         assert np.array_equal(got["s_x"].view(np.uint32), s2.view(np.uint32)), m
         assert np.array_equal(got["x_q"], q2), m
         assert np.array_equal(got["t"], oracle.lora_down(q2, prob.W_B)), m
+
+
+@pytest.mark.parametrize("B", [48, 96])
+@pytest.mark.parametrize("N,K", [(2048, 4096), (8512, 2048)], ids=["out_proj", "in_proj"])
+@pytest.mark.parametrize("form", ["one_call", "fused", "contract"])
+def test_mid_batches_every_problem(torch_cuda, B, N, K, form):
+    # The decode kernel's launch plan at batches that do not divide its resident group
+    # count (the 48-layer sweep's batch, and twice it): every group count per problem
+    # must still cover each problem's rows exactly once.  Every problem against the
+    # oracle, with the accumulators; then the instances without debug outputs must
+    # write the same y bytes.
+    import torch
+    from bit_scaffold_int8_amd.runner import DeviceProjections
+    probs = si.make_copies(1, N, K, 2, seed=7 * B + N, copies=B)
+    print(f"batch {B}, N {N}, K {K}, {form}", flush=True)
+    dp = DeviceProjections.from_problems(probs, with_acc=True)
+    run = {"one_call": dp.forward_one_call, "fused": dp.forward, "contract": dp.forward_contract}[form]
+    run()
+    torch.cuda.synchronize()
+    xq_all, acc_all, y_all = dp.x_q.cpu().numpy(), dp.acc_dbg.cpu().numpy(), dp.y.cpu().numpy()
+    for b, prob in enumerate(probs):
+        xq_ref, sx_ref = oracle.quantize_act(prob.x)
+        y_ref, acc_ref, t_ref = oracle.scaffold_lora_gemm(xq_ref, sx_ref, prob.P, prob.s_w, prob.W_A, prob.s_A,
+                                                          prob.W_B, prob.s_B, nthreads=16)
+        assert np.array_equal(xq_all[b], xq_ref), b
+        assert np.array_equal(acc_all[b], acc_ref), b
+        D = _magnitude(sx_ref, prob.s_w, acc_ref, prob.s_A, prob.W_A, prob.s_B, t_ref)
+        _assert_y(y_all[b], y_ref, D, f"problem {b}")
+    dp.y.fill_(float("nan"))
+    run(debug=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(dp.y.cpu().numpy().view(np.uint32), y_all.view(np.uint32)), "y without debug outputs"
