@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kHeadThreads) void int8_gemv_kernel(
     // row stride 20 words: the adds of one instruction (rows 4g+v, tokens i) hit
     // distinct banks
     __shared__ int32_t red[2][T * 16][20];
-    __shared__ float sxs[16];
+    __shared__ float sxs[kHeadThreads];  // token scales in the first M slots (one slot per thread)
 
     {
         const int64_t p = blockIdx.y;  // problem of a dense batch
@@ -88,17 +88,16 @@ __global__ __launch_bounds__(kHeadThreads) void int8_gemv_kernel(
             for (int c = 0; c < C; ++c) b.w[tt][c] = __builtin_amdgcn_raw_buffer_load_b128(e_rsrc, base + lane_off[c], 0, 0);
         }
     };
-    Stage s0, s1, s2;
-    load_stage(st_begin, s0);  // every group has at least one stage
-    load_stage(st_begin + 1 < st_end ? st_begin + 1 : st_end - 1, s1);
-
-    // the group's row scales (clamped rows past N are never stored)
+    // The small setup loads go out first, into registers: waits count loads in issue
+    // order, so the wait for them (before their LDS stores and the setup barrier) then
+    // leaves the first two weight stages in flight, instead of waiting for both to land
+    // and only then issuing the third.
+    // The group's row scales: one per thread (kHeadRowsCap == NT), rows clamped below N
+    // (clamped rows are never stored).
+    static_assert(kHeadRowsCap <= NT, "one row scale per thread");
     const int64_t row0 = st_begin * T * 16;
     const int nrows = (int)((st_end - st_begin) * T * 16);
-    for (int r = threadIdx.x; r < nrows; r += NT) {
-        const int64_t n = row0 + r;
-        se_lds[r] = s_e[n < N ? n : N - 1];
-    }
+    const float sev = s_e[row0 + threadIdx.x < N ? row0 + threadIdx.x : N - 1];
     // token i's codes for this lane's pieces (tokens past M and pieces past K: zero)
     v4i X[C];
     const uint8_t* xrow = reinterpret_cast<const uint8_t*>(x_q) + (i < M ? (int64_t)i * K : 0);
@@ -110,7 +109,16 @@ __global__ __launch_bounds__(kHeadThreads) void int8_gemv_kernel(
     }
     const float sxv = __uint_as_float(__float_as_uint(s_x[threadIdx.x < M ? threadIdx.x : 0]) &
                                       opaque_mask(threadIdx.x < M));
-    if (threadIdx.x < 16) sxs[threadIdx.x] = sxv;
+
+    Stage s0, s1, s2;
+    load_stage(st_begin, s0);  // every group has at least one stage
+    load_stage(st_begin + 1 < st_end ? st_begin + 1 : st_end - 1, s1);
+
+    // (every thread stores its slot, so neither load has a branch to sink into, where
+    // the wait for it would also wait for the stages; slots past the group's rows and
+    // past M tokens are never read)
+    se_lds[threadIdx.x] = sev;
+    sxs[threadIdx.x] = sxv;
     for (int q = threadIdx.x; q < 2 * T * 16 * 20; q += NT) (&red[0][0][0])[q] = 0;
     lds_barrier();
 
