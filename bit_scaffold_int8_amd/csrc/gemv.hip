@@ -791,7 +791,10 @@ static hipError_t launch_gemv_wct(bool fast, int setup, const int8_t* x_q, const
         const int64_t rounds = (batch * num_stages + resident_wgs * kMaxStages - 1) / (resident_wgs * kMaxStages);
         per_problem = (rounds * resident_wgs) / batch;
     } else {
-        const int64_t target_wgs = setup != kGivenT ? 256 : 2048;
+        // t given: ~8 groups per CU for one problem, ~2 per CU over a batch (at 2048 a
+        // batch of 48 out_proj problems got single-stage groups, whose loads never
+        // pipeline: 38.9 against 24.8 us; batch 8 in_proj 20.5 against 15.2 us)
+        const int64_t target_wgs = setup != kGivenT ? 256 : (batch > 1 ? 512 : 2048);
         per_problem = target_wgs / batch;
     }
     if (per_problem < 1) per_problem = 1;
