@@ -204,6 +204,20 @@ dfssm_status forward_impl(const float* x, int64_t M, int64_t N, int64_t K, const
         if (e != hipErrorNotSupported) return e == hipSuccess ? DFSSM_OK : DFSSM_ERR_HIP;
         // the launch plan has several groups per problem at a throughput batch: two kernels
     }
+    // Many-token projections with under 2^24 outputs per launch: the plain quantizer, then
+    // the MFMA kernel computing t from the code chunks it already stages (its first column
+    // tile writes t out).  Measured faster than quantize + LoRA-down followed by the product
+    // given t at every token count from 17 to 2048 for N = 2048, K = 4096 (1.2-2 us) and
+    // from 17 to 1536 for N = 8512, K = 2048 (up to 2.9 us); at 2048 tokens of the latter
+    // (2^24 outputs and more) the product is MFMA-bound and the W_B chunks every column
+    // tile recomputes cost more than the separate LoRA-down pass (1.1 us slower).  The
+    // bytes written are the same either way.
+    const bool decode_kernel = M <= kMaxDecodeM && K <= kGemvMaxK && gemv_fits;
+    if (rank == 16 && !decode_kernel && M * N * batch < ((int64_t)1 << 24) && dfssm::prefill_supported(M, N, K)) {
+        if (dfssm::launch_quantize_act(x, M * batch, K, x_q, s_x, stream) != hipSuccess) return DFSSM_ERR_HIP;
+        return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, w_b, s_b, nullptr, t, rank, y, acc_dbg, batch,
+                         stream);
+    }
     if (dfssm_status st = quantize_lora_down_impl(x, M, K, w_b, rank, x_q, s_x, t, batch, stream)) return st;
     return gemm_impl(x_q, s_x, M, N, K, w_bits, s_w, w_a, s_a, nullptr, s_b, t, nullptr, rank, y, acc_dbg, batch,
                      stream);

@@ -217,8 +217,11 @@ dfssm_status dfssm_scaffold_lora_gemm_given_t_strided_batched(const int8_t* x_q,
  * 8 up to 4096) -- e.g. M = 1, 2 at K = 4096 and K = 2048.  Every workgroup then
  * quantizes the tokens and computes t itself; the first workgroup of each problem
  * writes x_q, s_x and t.  Large batches that would spread one problem over several
- * workgroups (which would each redo that work), and all other shapes, take the two
- * kernels of the two-call form.
+ * workgroups (which would each redo that work), and all other shapes, take two
+ * kernels: at rank 16, shapes past the decode kernel (M > 16 or K > 16384) with
+ * M*N*batch < 2^24 and K % 64 == 0 the quantizer, then the product computing t in its
+ * K loop (the form dfssm_scaffold_lora_gemm runs), which writes t out as well; the
+ * rest those of the two-call form.
  * Requirements and errors are the union of the two calls'.
  */
 dfssm_status dfssm_scaffold_lora_forward(const float* x, int64_t M, int64_t N, int64_t K,

@@ -1,7 +1,9 @@
 """GPU parity of the one-call form (dfssm_scaffold_lora_forward): x -> x_q, s_x, t, y.
 
 At decode shapes it is one kernel whose every workgroup quantizes the tokens and
-computes t = W_B x_q itself; elsewhere it runs the two kernels of the two-call form.
+computes t = W_B x_q itself; elsewhere two kernels: for many-token shapes with under 2^24
+outputs the quantizer, then the MFMA product computing t in its K loop (which writes t
+out), otherwise those of the two-call form.
 Same bar as the rest: x_q, s_x, t and the accumulators bit-exact against the CPU
 oracle, y within 1e-5 of the magnitude of its terms; and y bit-identical to the
 two-call form's (both apply the same epilogue arithmetic to the same integers).
@@ -57,9 +59,13 @@ FUSED = [(1, 512, 128), (2, 100, 256), (4, 64, 256), (1, 333, 512), (2, 130, 102
          (2, 2048, 4096), (1, 8512, 2048), (2, 8512, 2048), (3, 1000, 1280), (1, 17, 384), (1, 1, 4096)]
 # two launches
 FALLBACK = [(4, 2048, 4096), (5, 300, 2048), (1, 200, 136), (1, 300, 8192), (16, 1000, 2048), (64, 700, 1024)]
+# many tokens: the quantizer, then the product computing t (ragged M and N, several K
+# tiles, N > K); K % 64 != 0 and 2^24 outputs or more keep the two-call form's kernels
+MANY = [(17, 2048, 4096), (200, 2048, 4096), (70, 96, 1088), (256, 1024, 1024), (33, 100, 136), (40, 600, 512),
+        (4100, 4096, 128)]
 
 
-@pytest.mark.parametrize("M,N,K", FUSED + FALLBACK)
+@pytest.mark.parametrize("M,N,K", FUSED + FALLBACK + MANY)
 def test_one_call_matches_oracle(torch_cuda, M, N, K):
     _check([si.make_problem(M, N, K, max(1, K // 512), seed=7 * M + N + K)])
 
@@ -71,7 +77,7 @@ def test_one_call_rank_zero(torch_cuda, M, N, K):
 
 # (64 out_proj copies: a throughput batch with several groups per problem, so two kernels)
 @pytest.mark.parametrize("B,M,N,K", [(3, 1, 2048, 4096), (5, 2, 8512, 2048), (7, 1, 40, 256), (4, 6, 100, 1024),
-                                     (64, 1, 2048, 4096)])
+                                     (64, 1, 2048, 4096), (3, 40, 256, 512), (2, 100, 2048, 4096)])
 def test_one_call_batched(torch_cuda, B, M, N, K):
     _check(si.make_copies(M, N, K, 2, seed=B * 100 + M, copies=B))
 
