@@ -33,7 +33,8 @@ def _run_hip(prob, with_acc=True, rank=16, path="fused"):
     'fused'    quantize_lora_down + gemm_given_t (batched entry points, batch 1);
     'unfused'  quantize_act, lora_down, gemm_given_t (single-problem entry points);
     'contract' quantize_act + scaffold_lora_gemm, which computes t itself (batched);
-    'contract_unfused' the same through the single-problem entry points."""
+    'contract_unfused' the same through the single-problem entry points;
+    'one_call' scaffold_lora_forward (batched entry point, batch 1)."""
     from bit_scaffold_int8_amd.runner import DeviceProjections
     import torch
     dp = DeviceProjections.from_problems([prob], rank=bool(rank), with_acc=with_acc)
@@ -45,6 +46,8 @@ def _run_hip(prob, with_acc=True, rank=16, path="fused"):
         dp.forward_contract()
     elif path == "contract_unfused":
         dp.forward_contract_unfused()
+    elif path == "one_call":
+        dp.forward_one_call()
     else:
         raise ValueError(path)
     torch.cuda.synchronize()

@@ -35,6 +35,16 @@ def test_prefill_config_parity(torch_cuda, monkeypatch, cfg, M, N, K, path):
     _check_full(si.make_problem(M, N, K, max(1, K // 100), seed=M * 31 + N * 7 + K + 5 * cfg), path=path)
 
 
+@pytest.mark.parametrize("cfg", CFGS)
+@pytest.mark.parametrize("M,N,K", [(129, 130, 4096), (300, 1000, 2112)])
+def test_prefill_config_one_call(torch_cuda, monkeypatch, cfg, M, N, K):
+    # the one-call form at these sizes runs the quantizer, then the product computing t,
+    # which writes t out from its first column tile (every configuration, and the
+    # generic kernel)
+    monkeypatch.setenv("DFSSM_PREFILL_CFG", str(cfg))
+    _check_full(si.make_problem(M, N, K, max(1, K // 100), seed=M + N + K + 3 * cfg), path="one_call")
+
+
 MAIN_TAIL = [(0, 1), (0, 2), (1, 2), (3, 5), (3, 6), (4, 5), (4, 6), (5, 6), (7, 8), (3, 4)]
 
 
