@@ -206,12 +206,12 @@ dfssm_status forward_impl(const float* x, int64_t M, int64_t N, int64_t K, const
     }
     // Many-token projections with under 2^24 outputs per launch: the plain quantizer, then
     // the MFMA kernel computing t from the code chunks it already stages (its first column
-    // tile writes t out).  Measured faster than quantize + LoRA-down followed by the product
-    // given t at every token count from 17 to 2048 for N = 2048, K = 4096 (1.2-2 us) and
-    // from 17 to 1536 for N = 8512, K = 2048 (up to 2.9 us); at 2048 tokens of the latter
-    // (2^24 outputs and more) the product is MFMA-bound and the W_B chunks every column
-    // tile recomputes cost more than the separate LoRA-down pass (1.1 us slower).  The
-    // bytes written are the same either way.
+    // tile writes t out).  Against quantize + LoRA-down followed by the product given t it
+    // measured 1.2-2 us faster from 17 to 2048 tokens for N = 2048, K = 4096, and level or
+    // up to 2.9 us faster from 17 to 1536 tokens for N = 8512, K = 2048.  At 2048 tokens of
+    // the latter (2^24 outputs and more) the product is MFMA-bound and the W_B chunks every
+    // column tile recomputes cost more than the separate LoRA-down pass (1.1 us slower).
+    // The bytes written are the same either way.
     const bool decode_kernel = M <= kMaxDecodeM && K <= kGemvMaxK && gemv_fits;
     if (rank == 16 && !decode_kernel && M * N * batch < ((int64_t)1 << 24) && dfssm::prefill_supported(M, N, K)) {
         if (dfssm::launch_quantize_act(x, M * batch, K, x_q, s_x, stream) != hipSuccess) return DFSSM_ERR_HIP;
