@@ -110,3 +110,27 @@ def test_one_call_outputs_only_from_first_group(torch_cuda):
     for o in outs[1:]:
         assert all(np.array_equal(a, b) for a, b in zip(o, outs[0]))
     _check(probs)
+
+
+def test_one_call_equals_two_call_form_on_random_shapes(torch_cuda):
+    # the one-call form promises the two-call form's results bit for bit, whichever
+    # kernels it takes: seeded random many-token shapes on both sides of the routing
+    # (ragged M and N, K with and without whole 64-k slices, batches), every output byte
+    # compared (x_q, s_x, t, y; no oracle needed for an identity between two paths)
+    import torch
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        M = int(rng.integers(1, 400))
+        N = int(rng.integers(1, 3000))
+        K = int(rng.choice([64, 136, 448, 1024, 2112, 4096]))
+        B = int(rng.integers(1, 4))
+        print(f"case {case}: B={B} M={M} N={N} K={K}", flush=True)
+        probs = si.make_copies(M, N, K, max(1, K // 512), seed=500 + case, copies=B)
+        one, two = _device(probs), _device(probs)
+        one.forward_one_call()
+        two.forward()
+        torch.cuda.synchronize()
+        for name in ("x_q", "s_x", "t", "y", "acc_dbg"):
+            a = getattr(one, name).cpu().numpy()
+            b = getattr(two, name).cpu().numpy()
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{name}, case {case}"
