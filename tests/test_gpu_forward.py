@@ -62,7 +62,7 @@ FALLBACK = [(4, 2048, 4096), (5, 300, 2048), (1, 200, 136), (1, 300, 8192), (16,
 # many tokens: the quantizer, then the product computing t (ragged M and N, several K
 # tiles, N > K); K % 64 != 0 and 2^24 outputs or more keep the two-call form's kernels
 MANY = [(17, 2048, 4096), (200, 2048, 4096), (70, 96, 1088), (256, 1024, 1024), (33, 100, 136), (40, 600, 512),
-        (4100, 4096, 128)]
+        (4100, 4096, 128), (2, 100, 20480)]  # the last: few tokens, K past the decode kernel's 16384
 
 
 @pytest.mark.parametrize("M,N,K", FUSED + FALLBACK + MANY)
